@@ -1,0 +1,143 @@
+"""Plain float64 definition of attention, of its masks by global position, and of the log-sum-exp merge.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): imported by the tests, the smoke check and the bench's
+CPU-baseline leg, never by the HIP path.
+
+Sources (page title, then the section on it):
+  [A] "深度学习注意力机制优化与FlashAttention实践", §2.1 数学表达式与计算流程 -- standard attention: scores are
+      Q times K transposed divided by sqrt(d_k), a softmax over the key axis, then a weighted sum of V.
+      Also "Mosaic多轴注意力分片：突破Transformer长序列处理瓶颈", §2.1 (the same formula).
+  [B] "架构层解决方案 - Sparse Attention与Ring Attention", section "Ring Attention / 核心创新" -- the softmax of a
+      full key set decomposes over key blocks once every block is shifted by one common maximum m.
+  [C] "分布式注意力机制突破：长序列处理的全景技术架构与实践指南", §2.2 stage 3 (pairwise LSE) and §3.4 (M-way
+      merge: common maximum over the parts, per-part sums rescaled to it, LSE = max + log of the sum).
+  [D] "深度学习注意力机制优化与FlashAttention实践", §5.1 -- causal masking must keep the autoregressive property.
+  [E] "注意力机制演进", timeline table, row "Striped Attention" (named only; defined here by position).
+  [F] "Mosaic多轴注意力分片：突破Transformer长序列处理瓶颈", §3.2 -- after all K/V shards have passed, each device
+      holds the complete attention output of its own query shard.
+
+Readings where the pages are silent or garbled (each also listed in the design notes):
+  * lse is the natural log of the sum of exp(scale * q.k) over the visible keys; no additive bias.
+  * The pairwise formula printed in [C] §2.2 has the wrong sign in the exponent; the correct identity is
+    log(e^a + e^b) = max(a, b) + log(1 + e^{-|a-b|}), which agrees with [C] §3.4's M-way steps.
+  * Causal is inclusive: a key at the same global position as the query is visible.
+  * Global positions: local query row i sits at q_off + i*stride, local key j at k_off + j*stride. Contiguous
+    shards use stride 1; striping over W devices uses stride W with q_off = r, k_off = s ([E], plainest reading).
+  * A query row with no visible key gets o = 0 and lse = -inf (no epsilon in the denominator); the merge treats
+    lse = -inf as weight zero.
+  * The scale is an explicit argument (the workloads pass 1/sqrt(d)).
+
+The attention here is the definition, not a blockwise algorithm: each query row's scores over ALL keys are
+materialised at once (rows are processed in chunks only to bound memory), so this code shares no structure with
+a tiled kernel.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+_CHUNK_ELEMS = 8 << 20   # at most ~64 MB of float64 scores per chunk
+
+
+def visible(nq: int, nk: int, causal: bool, q_off: int = 0, k_off: int = 0, stride: int = 1,
+            rows=None) -> np.ndarray:
+    """Boolean [R, nk]: True where key j is visible to query row i ([D], [E] and the position reading above).
+
+    rows: optional query row indices (default: all nq rows).
+    """
+    r = np.arange(nq, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    if not causal:
+        return np.ones((r.size, nk), dtype=bool)
+    q_pos = int(q_off) + int(stride) * r
+    k_pos = int(k_off) + int(stride) * np.arange(nk, dtype=np.int64)
+    return k_pos[None, :] <= q_pos[:, None]
+
+
+def _softmax_rows(s: np.ndarray, vis: np.ndarray):
+    """Row softmax of scores s over the visible entries; returns (p, lse). Empty rows: p = 0, lse = -inf."""
+    masked = np.where(vis, s, -np.inf)
+    m = masked.max(axis=-1, keepdims=True)                  # -inf for an empty row
+    has = np.isfinite(m)
+    shift = np.where(has, m, 0.0)
+    e = np.where(vis, np.exp(masked - shift), 0.0)
+    l = e.sum(axis=-1, keepdims=True)
+    with np.errstate(divide="ignore"):
+        lse = np.where(has, shift + np.log(l), -np.inf)
+    p = np.where(has, e / np.where(has, l, 1.0), 0.0)
+    return p, lse[..., 0]
+
+
+def attention(q, k, v, scale: float, causal: bool = False, q_off: int = 0, k_off: int = 0, stride: int = 1,
+              rows=None):
+    """Exact attention ([A]) with the mask by global position, in float64.
+
+    q: [B, H, Nq, d]; k: [B, H, Nk, d]; v: [B, H, Nk, dv] (any real dtype; widened to float64).
+    rows: optional 1-D indices of the query rows to compute (the same rows for every batch and head). Every
+          output row depends only on its own query row and all keys, so a subset is exact.
+    Returns (o [B, H, R, dv] float64, lse [B, H, R] float64), lse in natural log.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if k.shape[:2] != (B, H) or v.shape[:3] != (B, H, Nk) or k.shape[3] != d:
+        raise ValueError("shape mismatch")
+    rows = np.arange(Nq, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    R = rows.size
+    o = np.zeros((B, H, R, v.shape[3]), dtype=np.float64)
+    lse = np.full((B, H, R), -np.inf, dtype=np.float64)
+    chunk = max(1, _CHUNK_ELEMS // max(1, Nk))
+    for c0 in range(0, R, chunk):
+        rr = rows[c0:c0 + chunk]
+        vis = visible(Nq, Nk, causal, q_off, k_off, stride, rows=rr)
+        for b in range(B):
+            for h in range(H):
+                s = scale * (q[b, h, rr] @ k[b, h].T)       # [r, Nk] scores, scaled ([A])
+                p, l = _softmax_rows(s, vis)
+                o[b, h, c0:c0 + rr.size] = p @ v[b, h]
+                lse[b, h, c0:c0 + rr.size] = l
+    return o, lse
+
+
+def lse_merge_many(parts):
+    """Merge partial results [(o_i, lse_i), ...] computed over disjoint key sets ([B], [C] §3.4).
+
+    With lse_i = m_i + log s_i (local maximum m_i, local shifted sum s_i), [C] §3.4 takes the common maximum
+    m = max_i m_i, the merged sum s = sum_i s_i * exp(m_i - m) and LSE = m + log s. In terms of the stored lse_i
+    this is s = sum_i exp(lse_i - m) with m = max_i lse_i; each part's output is weighted by its share
+    exp(lse_i - LSE) of the merged normaliser ([B]). Parts with lse = -inf (no visible key) weigh zero; if every
+    part is empty the result is (0, -inf).
+    """
+    os_ = [np.asarray(o, dtype=np.float64) for o, _ in parts]
+    ls = [np.asarray(l, dtype=np.float64) for _, l in parts]
+    m = ls[0]
+    for l in ls[1:]:
+        m = np.maximum(m, l)
+    has = np.isfinite(m)
+    shift = np.where(has, m, 0.0)
+    w = [np.where(np.isfinite(l), np.exp(l - shift), 0.0) for l in ls]
+    s = sum(w)
+    with np.errstate(divide="ignore"):
+        lse = np.where(has, shift + np.log(np.where(has, s, 1.0)), -np.inf)
+    den = np.where(has, s, 1.0)[..., None]
+    o = sum(wi[..., None] * oi for wi, oi in zip(w, os_)) / den
+    o = np.where(has[..., None], o, 0.0)
+    return o, lse
+
+
+def lse_merge(o_a, lse_a, o_b, lse_b):
+    """Merge two partials (the two-part case of lse_merge_many)."""
+    return lse_merge_many([(o_a, lse_a), (o_b, lse_b)])
+
+
+def lse_pair(a, b):
+    """log(e^a + e^b) by the pairwise form of [C] §2.2 with its exponent sign corrected:
+    max(a, b) + log(1 + e^{-|a-b|}); -inf if both are -inf."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    m = np.maximum(a, b)
+    both_empty = np.isneginf(m)
+    with np.errstate(invalid="ignore"):
+        diff = np.abs(a - b)                    # +inf when exactly one side is -inf: the term below is 0
+        out = m + np.log1p(np.exp(-diff))
+    return np.where(both_empty, -np.inf, out)
