@@ -1,0 +1,249 @@
+"""Python binding of libebattn (exact blockwise attention and the log-sum-exp merge on MI355X).
+
+Argument marshalling only: every step of the computation runs in the library's HIP kernels. PyTorch provides
+device memory (outputs are allocated with ``torch.empty`` when not given) and the stream (the current torch
+stream of the tensors' device). Importing this package fails loudly if the shared library is not built; there
+is no fallback implementation.
+
+Names and semantics follow the C ABI in include/ebattn.h:
+
+    o, lse = attn_fwd(q, k, v, scale=..., causal=..., q_off=..., k_off=..., pos_stride=...)
+    o, lse = attn_lse_merge(o_a, lse_a, o_b, lse_b)
+    o, lse = ring_local(q_shard, [(k0, v0, k_off0), (k1, v1, k_off1), ...], scale=..., causal=..., q_off=...)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+from typing import List, Optional, Sequence, Tuple
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libebattn.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "ebattn.h")
+
+ATTN_OK = 0
+ATTN_EINVAL = -1
+ATTN_EUNSUPPORTED = -2
+ATTN_EHIP = -3
+ATTN_EWORKSPACE = -4
+ATTN_F32 = 0
+ATTN_BF16 = 1
+ATTN_MAX_SEQ = 1 << 28
+
+
+class AttnError(RuntimeError):
+    """A non-zero status returned by the library, with its attn_last_error() message."""
+
+    def __init__(self, code: int, message: str):
+        super().__init__(f"ebattn error {code}: {message}")
+        self.code = code
+        self.message = message
+
+
+class KVBlock(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("Nk", ctypes.c_int), ("k_off", ctypes.c_int64)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m exact_blockwise_attention_amd.build` "
+                          "(there is no fallback implementation)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, I64, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    lib.attn_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I64, I64, I, I, I, P]
+    lib.attn_fwd.restype = I
+    lib.attn_lse_merge.argtypes = [P, P, P, P, P, P, I64, I, I, I, P]
+    lib.attn_lse_merge.restype = I
+    lib.ring_local.argtypes = [P, ctypes.POINTER(KVBlock), I, P, P, I, I, I, I, F, I, I64, I, I, I, P, SZ, P]
+    lib.ring_local.restype = I
+    lib.ring_local_workspace_bytes.argtypes = [I, I, I, I]
+    lib.ring_local_workspace_bytes.restype = SZ
+    lib.ring_local_plan.argtypes = [ctypes.POINTER(KVBlock), I, I, I, I64, I, ctypes.POINTER(I)]
+    lib.ring_local_plan.restype = I
+    lib.attn_last_error.argtypes = []
+    lib.attn_last_error.restype = ctypes.c_char_p
+    lib.attn_version.argtypes = []
+    lib.attn_version.restype = I
+    return lib
+
+
+lib = _load()
+
+
+def declared_symbols() -> List[str]:
+    """Names of the functions declared in include/ebattn.h."""
+    with open(HEADER_PATH, encoding="utf-8") as f:
+        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+
+
+def last_error() -> str:
+    return (lib.attn_last_error() or b"").decode("utf-8", "replace")
+
+
+def _check(rc: int):
+    if rc != ATTN_OK:
+        raise AttnError(rc, last_error())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _code(dtype) -> int:
+    torch = _torch()
+    if dtype == torch.bfloat16:
+        return ATTN_BF16
+    if dtype == torch.float32:
+        return ATTN_F32
+    raise TypeError(f"unsupported dtype {dtype} (bfloat16 or float32)")
+
+
+def _ptr(t) -> Optional[int]:
+    return t.data_ptr() if t is not None and t.numel() > 0 else None
+
+
+def _stream(t) -> int:
+    return _torch().cuda.current_stream(t.device).cuda_stream
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("tensors must be on a GPU device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    dev = {t.device for t in ts if t is not None}
+    if len(dev) > 1:
+        raise ValueError("tensors are on different devices")
+
+
+def version() -> int:
+    return lib.attn_version()
+
+
+def attn_fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False, q_off: int = 0, k_off: int = 0,
+             pos_stride: int = 1, out=None, lse=None, out_dtype=None) -> Tuple[object, object]:
+    """Exact attention of q [B,H,Nq,d] against k, v [B,H,Nk,d]; returns (o [B,H,Nq,d], lse [B,H,Nq] fp32).
+
+    scale defaults to 1/sqrt(d). Causal masking is by global position (q_off + i*pos_stride vs
+    k_off + j*pos_stride, inclusive). out_dtype defaults to q.dtype.
+    """
+    torch = _torch()
+    _need_cuda(q, k, v, out, lse)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if tuple(k.shape) != (B, H, Nk, d) or tuple(v.shape) != (B, H, Nk, d):
+        raise ValueError("k and v must be [B, H, Nk, d] with q's B, H, d")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share a dtype")
+    out_dtype = out_dtype or (out.dtype if out is not None else q.dtype)
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if tuple(out.shape) != (B, H, Nq, d) or tuple(lse.shape) != (B, H, Nq) or lse.dtype != torch.float32:
+        raise ValueError("out must be [B,H,Nq,d] and lse fp32 [B,H,Nq]")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _check(lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, d, scale, int(causal),
+                        int(q_off), int(k_off), int(pos_stride), _code(q.dtype), _code(out.dtype), _stream(q)))
+    return out, lse
+
+
+def attn_lse_merge(o_a, lse_a, o_b, lse_b, *, out=None, lse_out=None, out_dtype=None) -> Tuple[object, object]:
+    """Merges two partials over disjoint key sets; o_* are [..., d], lse_* the matching [...] fp32.
+
+    out may be o_a or o_b (same dtype) and lse_out may be lse_a or lse_b for an in-place merge.
+    """
+    torch = _torch()
+    _need_cuda(o_a, lse_a, o_b, lse_b, out, lse_out)
+    if o_a.shape != o_b.shape or o_a.dtype != o_b.dtype:
+        raise ValueError("o_a and o_b must match in shape and dtype")
+    if lse_a.shape != o_a.shape[:-1] or lse_b.shape != o_a.shape[:-1]:
+        raise ValueError("lse_a/lse_b must have o's shape without the last axis")
+    if lse_a.dtype != torch.float32 or lse_b.dtype != torch.float32:
+        raise TypeError("lse tensors must be fp32")
+    d = o_a.shape[-1]
+    rows = o_a.numel() // d if d else 0
+    out_dtype = out_dtype or (out.dtype if out is not None else o_a.dtype)
+    if out is None:
+        out = torch.empty(o_a.shape, dtype=out_dtype, device=o_a.device)
+    if lse_out is None:
+        lse_out = torch.empty(lse_a.shape, dtype=torch.float32, device=o_a.device)
+    if out.shape != o_a.shape or lse_out.shape != lse_a.shape:
+        raise ValueError("out / lse_out shapes do not match the partials")
+    _check(lib.attn_lse_merge(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(out), _ptr(lse_out), rows, d,
+                              _code(o_a.dtype), _code(out.dtype), _stream(o_a)))
+    return out, lse_out
+
+
+def ring_local_workspace_bytes(B: int, H: int, Nq: int, d: int) -> int:
+    return int(lib.ring_local_workspace_bytes(B, H, Nq, d))
+
+
+def _blocks(kv_blocks) -> Tuple[ctypes.Array, int]:
+    arr = (KVBlock * max(1, len(kv_blocks)))()
+    for i, (k, v, k_off) in enumerate(kv_blocks):
+        if hasattr(k, "data_ptr"):
+            arr[i] = KVBlock(_ptr(k), _ptr(v), int(k.shape[2]), int(k_off))
+        else:  # (k_ptr, v_ptr, Nk, k_off) raw form is not accepted here; use explicit ints via KVBlock
+            raise TypeError("kv_blocks entries are (k, v, k_off) with k, v tensors")
+    return arr, len(kv_blocks)
+
+
+def ring_local_plan(Nq: int, blocks: Sequence[Tuple[int, int]], *, causal: bool, q_off: int = 0,
+                    pos_stride: int = 1) -> Tuple[int, List[int]]:
+    """Host-only: classifies blocks given as (Nk, k_off). Returns (live count, kinds) with kinds 0 = skipped,
+    1 = fully visible, 2 = partly visible."""
+    arr = (KVBlock * max(1, len(blocks)))()
+    for i, (nk, ko) in enumerate(blocks):
+        arr[i] = KVBlock(None, None, int(nk), int(ko))
+    kinds = (ctypes.c_int * max(1, len(blocks)))()
+    live = lib.ring_local_plan(arr, len(blocks), int(Nq), int(causal), int(q_off), int(pos_stride), kinds)
+    if live < 0:
+        raise AttnError(live, last_error())
+    return live, [kinds[i] for i in range(len(blocks))]
+
+
+def ring_local(q_shard, kv_blocks, *, scale: Optional[float] = None, causal: bool = False, q_off: int = 0,
+               pos_stride: int = 1, out=None, lse=None, out_dtype=None, workspace=None) -> Tuple[object, object]:
+    """One device's share of Ring Attention: q_shard [B,H,Nq,d] against kv_blocks = [(k, v, k_off), ...]
+    processed in the given (ring) order and merged; returns (o, lse) of attention over all blocks.
+
+    workspace: optional uint8 device tensor of at least ring_local_workspace_bytes(B, H, Nq, d) bytes;
+    allocated here when needed and not given.
+    """
+    torch = _torch()
+    _need_cuda(q_shard, out, lse, workspace)
+    for k, v, _ in kv_blocks:
+        _need_cuda(q_shard, k, v)
+        if k.dtype != q_shard.dtype or v.dtype != q_shard.dtype:
+            raise TypeError("blocks must share the query dtype")
+        if k.shape[:2] != q_shard.shape[:2] or k.shape != v.shape or k.shape[3] != q_shard.shape[3]:
+            raise ValueError("each block is k, v [B, H, Nk, d] with the query's B, H, d")
+    B, H, Nq, d = q_shard.shape
+    out_dtype = out_dtype or (out.dtype if out is not None else q_shard.dtype)
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=out_dtype, device=q_shard.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q_shard.device)
+    live, _ = ring_local_plan(Nq, [(k.shape[2], ko) for k, _, ko in kv_blocks], causal=causal, q_off=q_off,
+                              pos_stride=pos_stride)
+    need = ring_local_workspace_bytes(B, H, Nq, d)
+    if workspace is None and live > 1:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_shard.device)
+    arr, n = _blocks(kv_blocks)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.ring_local(_ptr(q_shard), arr, n, _ptr(out), _ptr(lse), B, H, Nq, d, scale, int(causal), int(q_off),
+                          int(pos_stride), _code(q_shard.dtype), _code(out.dtype), ws_ptr, ws_bytes,
+                          _stream(q_shard)))
+    return out, lse

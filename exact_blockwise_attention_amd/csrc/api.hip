@@ -1,0 +1,333 @@
+// C ABI of the library: argument validation, mask-to-diagonal reduction, kernel dispatch and the ring_local
+// driver. Every check runs on the host before the first HIP call, so argument errors never touch the device.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/ebattn.h"
+#include "internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(ATTN_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Span {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+Span span(const void* p, int64_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Span{lo, lo + (uintptr_t)(bytes > 0 ? bytes : 0)};
+}
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
+
+int64_t elem_bytes(int dtype) { return dtype == ATTN_F32 ? 4 : 2; }
+
+bool dtype_ok(int t) { return t == ATTN_F32 || t == ATTN_BF16; }
+bool head_dim_ok(int d) { return d == 24 || d == 64 || d == 128; }
+
+// "key j visible to query i" <=> k_off + j*s <= q_off + i*s <=> j <= i + floor((q_off - k_off) / s).
+// Clamped so that every int32 expression in the kernels stays in range; with Nq, Nk <= 2^28 the clamp never
+// changes which keys are visible.
+int diag_offset(int64_t q_off, int64_t k_off, int s) {
+  const int64_t num = q_off - k_off;
+  int64_t dq = num / s;
+  if ((num % s != 0) && (num < 0)) dq -= 1;  // floor division
+  const int64_t lim = (int64_t)1 << 29;
+  if (dq > lim) dq = lim;
+  if (dq < -lim) dq = -lim;
+  return (int)dq;
+}
+
+const int64_t kOffLimit = (int64_t)1 << 62;
+
+// Common validation of a query-side call. Returns ATTN_OK or an error code (message set).
+int check_query_side(const void* q, const void* o, const float* lse, int B, int H, int Nq, int d, float scale,
+                     int causal, int64_t q_off, int pos_stride, int in_dtype, int o_dtype) {
+  if (B < 0 || H < 0 || Nq < 0) return fail(ATTN_EINVAL, "negative size (B=%d H=%d Nq=%d)", B, H, Nq);
+  if (Nq > ATTN_MAX_SEQ) return fail(ATTN_EINVAL, "Nq=%d exceeds ATTN_MAX_SEQ", Nq);
+  if (!(causal == 0 || causal == 1)) return fail(ATTN_EINVAL, "causal must be 0 or 1 (got %d)", causal);
+  if (pos_stride < 1) return fail(ATTN_EINVAL, "pos_stride must be >= 1 (got %d)", pos_stride);
+  if (!(scale > 0.0f) || !isfinite(scale)) return fail(ATTN_EINVAL, "scale must be finite and > 0");
+  if (q_off > kOffLimit || q_off < -kOffLimit) return fail(ATTN_EINVAL, "q_off out of range");
+  if (!dtype_ok(in_dtype) || !dtype_ok(o_dtype)) return fail(ATTN_EINVAL, "unknown dtype code");
+  if (in_dtype == ATTN_F32 && o_dtype != ATTN_F32)
+    return fail(ATTN_EUNSUPPORTED, "fp32 inputs require an fp32 output");
+  if (!head_dim_ok(d)) return fail(ATTN_EUNSUPPORTED, "head dim d=%d not supported (24, 64, 128)", d);
+  const int64_t rows = (int64_t)B * H * Nq;
+  if (rows == 0) return ATTN_OK;
+  if (!q || !o || !lse) return fail(ATTN_EINVAL, "null q, o or lse pointer");
+  if (!aligned(q, 16) || !aligned(o, 16)) return fail(ATTN_EINVAL, "q and o must be 16-byte aligned");
+  if (!aligned(lse, 4)) return fail(ATTN_EINVAL, "lse must be 4-byte aligned");
+  return ATTN_OK;
+}
+
+int check_kv(const void* k, const void* v, int64_t BH, int Nk, int d, int in_dtype, int64_t k_off,
+             const void* q, const void* o, const float* lse, int64_t Nq, int o_dtype) {
+  if (Nk < 0) return fail(ATTN_EINVAL, "negative Nk=%d", Nk);
+  if (Nk > ATTN_MAX_SEQ) return fail(ATTN_EINVAL, "Nk=%d exceeds ATTN_MAX_SEQ", Nk);
+  if (k_off > kOffLimit || k_off < -kOffLimit) return fail(ATTN_EINVAL, "k_off out of range");
+  if (Nk == 0 || BH == 0) return ATTN_OK;
+  if (!k || !v) return fail(ATTN_EINVAL, "null k or v pointer");
+  if (!aligned(k, 16) || !aligned(v, 16)) return fail(ATTN_EINVAL, "k and v must be 16-byte aligned");
+  const int64_t kvb = BH * Nk * d * elem_bytes(in_dtype);
+  const Span so = span(o, BH * Nq * d * elem_bytes(o_dtype)), sl = span(lse, BH * Nq * 4);
+  if (overlap(so, span(k, kvb)) || overlap(so, span(v, kvb)) || overlap(sl, span(k, kvb)) ||
+      overlap(sl, span(v, kvb)))
+    return fail(ATTN_EINVAL, "o/lse overlap k or v");
+  (void)q;
+  return ATTN_OK;
+}
+
+int check_outputs_disjoint(const void* q, const void* o, const float* lse, int64_t rows, int d, int in_dtype,
+                           int o_dtype) {
+  const Span sq = span(q, rows * d * elem_bytes(in_dtype));
+  const Span so = span(o, rows * d * elem_bytes(o_dtype));
+  const Span sl = span(lse, rows * 4);
+  if (overlap(so, sq) || overlap(sl, sq) || overlap(so, sl)) return fail(ATTN_EINVAL, "o/lse overlap q or each other");
+  return ATTN_OK;
+}
+
+// Enqueue one attention forward whose arguments have been validated.
+int enqueue_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t BH, int Nq, int Nk,
+                int d, float scale, int causal, int diag, int in_dtype, int o_dtype, hipStream_t stream) {
+  const int64_t rows = BH * Nq;
+  if (rows == 0) return ATTN_OK;
+  const bool all_hidden = (Nk == 0) || (causal && (int64_t)Nq - 1 + diag < 0);
+  hipError_t e;
+  if (all_hidden) {
+    e = ebattn::launch_fill_empty(o, lse, rows, d, o_dtype == ATTN_F32, stream);
+    return e == hipSuccess ? ATTN_OK : hip_fail(e, "fill launch");
+  }
+  ebattn::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.BH = BH;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.causal = causal;
+  a.diag = diag;
+  if (in_dtype == ATTN_F32)
+    e = ebattn::launch_attn_fwd_f32(a, d, stream);
+  else if (Nq <= ebattn::kShortMax && Nk <= ebattn::kShortMax)
+    e = ebattn::launch_attn_fwd_short(a, d, o_dtype == ATTN_F32, stream);
+  else
+    e = ebattn::launch_attn_fwd_bf16(a, d, o_dtype == ATTN_F32, stream);
+  return e == hipSuccess ? ATTN_OK : hip_fail(e, "attention launch");
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int classify(int Nq, int Nk, int causal, int64_t q_off, int64_t k_off, int s) {
+  if (Nk <= 0 || Nq <= 0) return 0;
+  if (!causal) return 1;
+  const int diag = diag_offset(q_off, k_off, s);
+  if ((int64_t)Nq - 1 + diag < 0) return 0;   // even the last query row sees no key
+  if ((int64_t)diag >= (int64_t)Nk - 1) return 1;  // even the first query row sees every key
+  return 2;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_last_error(void) { return g_err; }
+
+int attn_version(void) { return 100; }
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk, int d,
+             float scale, int causal, int64_t q_off, int64_t k_off, int pos_stride, int in_dtype, int o_dtype,
+             void* stream) {
+  g_err[0] = '\0';
+  int rc = check_query_side(q, o, lse, B, H, Nq, d, scale, causal, q_off, pos_stride, in_dtype, o_dtype);
+  if (rc != ATTN_OK) return rc;
+  const int64_t BH = (int64_t)B * H;
+  rc = check_kv(k, v, BH, Nk, d, in_dtype, k_off, q, o, lse, Nq, o_dtype);
+  if (rc != ATTN_OK) return rc;
+  if (BH * Nq == 0) return ATTN_OK;
+  rc = check_outputs_disjoint(q, o, lse, BH * Nq, d, in_dtype, o_dtype);
+  if (rc != ATTN_OK) return rc;
+  (void)hipGetLastError();  // drop a stale error so a failure below is attributed to this call
+  return enqueue_fwd(q, k, v, o, lse, BH, Nq, Nk, d, scale, causal, diag_offset(q_off, k_off, pos_stride),
+                     in_dtype, o_dtype, reinterpret_cast<hipStream_t>(stream));
+}
+
+int attn_lse_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b, void* o, float* lse,
+                   int64_t rows, int d, int part_dtype, int o_dtype, void* stream) {
+  g_err[0] = '\0';
+  if (rows < 0) return fail(ATTN_EINVAL, "negative rows");
+  if (d <= 0) return fail(ATTN_EINVAL, "d must be > 0");
+  if (!dtype_ok(part_dtype) || !dtype_ok(o_dtype)) return fail(ATTN_EINVAL, "unknown dtype code");
+  const int vec = part_dtype == ATTN_F32 ? 4 : 8;
+  if (d % vec != 0 || d > 64 * vec)
+    return fail(ATTN_EUNSUPPORTED, "d=%d must be a multiple of %d and at most %d", d, vec, 64 * vec);
+  if (rows == 0) return ATTN_OK;
+  if (!o_a || !lse_a || !o_b || !lse_b || !o || !lse) return fail(ATTN_EINVAL, "null pointer");
+  if (!aligned(o_a, 16) || !aligned(o_b, 16) || !aligned(o, 16)) return fail(ATTN_EINVAL, "o_a, o_b, o not 16-byte aligned");
+  if (!aligned(lse_a, 4) || !aligned(lse_b, 4) || !aligned(lse, 4)) return fail(ATTN_EINVAL, "lse not 4-byte aligned");
+  const int64_t pb = rows * d * elem_bytes(part_dtype), ob = rows * d * elem_bytes(o_dtype), lb = rows * 4;
+  const Span sa = span(o_a, pb), sb = span(o_b, pb), so = span(o, ob);
+  const Span sla = span(lse_a, lb), slb = span(lse_b, lb), sl = span(lse, lb);
+  const bool o_in_place = (o == o_a || o == o_b) && o_dtype == part_dtype;
+  if (!o_in_place && (overlap(so, sa) || overlap(so, sb)))
+    return fail(ATTN_EINVAL, "o overlaps o_a/o_b without being exactly one of them (same dtype)");
+  if (o == o_a && o == o_b) return fail(ATTN_EINVAL, "o_a and o_b are the same buffer as o");
+  const bool l_in_place = (lse == lse_a || lse == lse_b);
+  if (!l_in_place && (overlap(sl, sla) || overlap(sl, slb)))
+    return fail(ATTN_EINVAL, "lse overlaps lse_a/lse_b without being exactly one of them");
+  if (overlap(so, sl) || overlap(so, sla) || overlap(so, slb) || overlap(sl, sa) || overlap(sl, sb))
+    return fail(ATTN_EINVAL, "an output overlaps a buffer of the other kind");
+  ebattn::MergeArgs a;
+  a.o_a = o_a;
+  a.lse_a = lse_a;
+  a.o_b = o_b;
+  a.lse_b = lse_b;
+  a.o = o;
+  a.lse = lse;
+  a.rows = rows;
+  a.d = d;
+  (void)hipGetLastError();
+  const hipError_t e = ebattn::launch_lse_merge(a, part_dtype == ATTN_F32, o_dtype == ATTN_F32,
+                                                reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : hip_fail(e, "merge launch");
+}
+
+size_t ring_local_workspace_bytes(int B, int H, int Nq, int d) {
+  if (B < 0 || H < 0 || Nq < 0 || d < 0) return 0;
+  const size_t rows = (size_t)B * H * Nq;
+  return 2 * (align256(rows * d * 4) + align256(rows * 4));
+}
+
+int ring_local_plan(const attn_kv_block* kv_blocks, int n_blocks, int Nq, int causal, int64_t q_off, int pos_stride,
+                    int* kinds) {
+  g_err[0] = '\0';
+  if (n_blocks < 0) return fail(ATTN_EINVAL, "negative n_blocks");
+  if (n_blocks > 0 && (!kv_blocks || !kinds)) return fail(ATTN_EINVAL, "null kv_blocks or kinds");
+  if (Nq < 0) return fail(ATTN_EINVAL, "negative Nq");
+  if (!(causal == 0 || causal == 1)) return fail(ATTN_EINVAL, "causal must be 0 or 1");
+  if (pos_stride < 1) return fail(ATTN_EINVAL, "pos_stride must be >= 1");
+  if (q_off > kOffLimit || q_off < -kOffLimit) return fail(ATTN_EINVAL, "q_off out of range");
+  int live = 0;
+  for (int i = 0; i < n_blocks; ++i) {
+    const attn_kv_block& b = kv_blocks[i];
+    if (b.Nk < 0 || b.Nk > ATTN_MAX_SEQ) return fail(ATTN_EINVAL, "block %d: bad Nk=%d", i, b.Nk);
+    if (b.k_off > kOffLimit || b.k_off < -kOffLimit) return fail(ATTN_EINVAL, "block %d: k_off out of range", i);
+    kinds[i] = classify(Nq, b.Nk, causal, q_off, b.k_off, pos_stride);
+    live += kinds[i] != 0;
+  }
+  return live;
+}
+
+int ring_local(const void* q_shard, const attn_kv_block* kv_blocks, int n_blocks, void* o, float* lse, int B, int H,
+               int Nq, int d, float scale, int causal, int64_t q_off, int pos_stride, int in_dtype, int o_dtype,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = '\0';
+  int rc = check_query_side(q_shard, o, lse, B, H, Nq, d, scale, causal, q_off, pos_stride, in_dtype, o_dtype);
+  if (rc != ATTN_OK) return rc;
+  if (n_blocks < 0) return fail(ATTN_EINVAL, "negative n_blocks");
+  if (n_blocks > 0 && !kv_blocks) return fail(ATTN_EINVAL, "null kv_blocks");
+  const int64_t BH = (int64_t)B * H;
+  const int64_t rows = BH * Nq;
+  for (int i = 0; i < n_blocks; ++i) {
+    rc = check_kv(kv_blocks[i].k, kv_blocks[i].v, BH, kv_blocks[i].Nk, d, in_dtype, kv_blocks[i].k_off, q_shard, o,
+                  lse, Nq, o_dtype);
+    if (rc != ATTN_OK) {
+      char msg[512];
+      snprintf(msg, sizeof(msg), "block %d: %s", i, g_err);
+      return fail(rc, "%s", msg);
+    }
+  }
+  if (rows == 0) return ATTN_OK;
+  rc = check_outputs_disjoint(q_shard, o, lse, rows, d, in_dtype, o_dtype);
+  if (rc != ATTN_OK) return rc;
+
+  // Host plan: which blocks can contribute at all.
+  int live = 0;
+  for (int i = 0; i < n_blocks; ++i)
+    live += classify(Nq, kv_blocks[i].Nk, causal, q_off, kv_blocks[i].k_off, pos_stride) != 0;
+
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (live >= 2) {
+    const size_t need = ring_local_workspace_bytes(B, H, Nq, d);
+    if (!workspace || workspace_bytes < need)
+      return fail(ATTN_EWORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 256)) return fail(ATTN_EINVAL, "workspace must be 256-byte aligned");
+    const Span sw = span(workspace, (int64_t)need);
+    if (overlap(sw, span(o, rows * d * elem_bytes(o_dtype))) || overlap(sw, span(lse, rows * 4)) ||
+        overlap(sw, span(q_shard, rows * d * elem_bytes(in_dtype))))
+      return fail(ATTN_EINVAL, "workspace overlaps q, o or lse");
+    for (int i = 0; i < n_blocks; ++i) {
+      const int64_t kvb = BH * kv_blocks[i].Nk * d * elem_bytes(in_dtype);
+      if (kv_blocks[i].Nk > 0 && (overlap(sw, span(kv_blocks[i].k, kvb)) || overlap(sw, span(kv_blocks[i].v, kvb))))
+        return fail(ATTN_EINVAL, "workspace overlaps block %d", i);
+    }
+  }
+  (void)hipGetLastError();  // drop a stale error so a failure below is attributed to this call
+  if (live == 0) {
+    const hipError_t e = ebattn::launch_fill_empty(o, lse, rows, d, o_dtype == ATTN_F32, st);
+    return e == hipSuccess ? ATTN_OK : hip_fail(e, "fill launch");
+  }
+  if (live == 1) {
+    for (int i = 0; i < n_blocks; ++i) {
+      const attn_kv_block& b = kv_blocks[i];
+      if (classify(Nq, b.Nk, causal, q_off, b.k_off, pos_stride) == 0) continue;
+      return enqueue_fwd(q_shard, b.k, b.v, o, lse, BH, Nq, b.Nk, d, scale, causal,
+                         diag_offset(q_off, b.k_off, pos_stride), in_dtype, o_dtype, st);
+    }
+  }
+
+  char* ws = reinterpret_cast<char*>(workspace);
+  float* acc_o = reinterpret_cast<float*>(ws);
+  float* acc_l = reinterpret_cast<float*>(ws + align256(rows * d * 4));
+  float* part_o = reinterpret_cast<float*>(ws + align256(rows * d * 4) + align256(rows * 4));
+  float* part_l = reinterpret_cast<float*>(ws + 2 * align256(rows * d * 4) + align256(rows * 4));
+
+  int done = 0;
+  for (int i = 0; i < n_blocks; ++i) {
+    const attn_kv_block& b = kv_blocks[i];
+    if (classify(Nq, b.Nk, causal, q_off, b.k_off, pos_stride) == 0) continue;
+    const int diag = diag_offset(q_off, b.k_off, pos_stride);
+    if (done == 0) {
+      rc = enqueue_fwd(q_shard, b.k, b.v, acc_o, acc_l, BH, Nq, b.Nk, d, scale, causal, diag, in_dtype, ATTN_F32, st);
+      if (rc != ATTN_OK) return rc;
+    } else {
+      rc = enqueue_fwd(q_shard, b.k, b.v, part_o, part_l, BH, Nq, b.Nk, d, scale, causal, diag, in_dtype, ATTN_F32, st);
+      if (rc != ATTN_OK) return rc;
+      const bool last = (done == live - 1);
+      ebattn::MergeArgs m;
+      m.o_a = acc_o;
+      m.lse_a = acc_l;
+      m.o_b = part_o;
+      m.lse_b = part_l;
+      m.o = last ? o : acc_o;
+      m.lse = last ? lse : acc_l;
+      m.rows = rows;
+      m.d = d;
+      const hipError_t e = ebattn::launch_lse_merge(m, 1, last ? (o_dtype == ATTN_F32) : 1, st);
+      if (e != hipSuccess) return hip_fail(e, "merge launch");
+    }
+    ++done;
+  }
+  return ATTN_OK;
+}
+
+}  // extern "C"

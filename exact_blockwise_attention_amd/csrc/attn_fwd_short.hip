@@ -1,0 +1,131 @@
+// Exact attention forward for short sequences (at most 16 queries and 16 keys per (batch, head) slice),
+// bf16 operands, fp32 arithmetic.
+//
+// The multi-axis layout of "Mosaic多轴注意力分片：突破Transformer长序列处理瓶颈" §2.2/§3.1 attends over a small
+// axis (a handful of features) for every row of a huge table: millions of independent tiny slices. Tiling
+// one slice onto MFMA would waste almost all of it, and the job is HBM-bound anyway, so a workgroup takes
+// many consecutive slices at once: it copies their K and V (contiguous in memory) into LDS with 16-byte
+// coalesced loads, then every lane computes one query row exactly (all scores, max, exp, sum, weighted
+// sum of V) in fp32.
+#include "internal.h"
+
+namespace ebattn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kThreads = 256;
+
+template <int D, bool OF32>
+__global__ __launch_bounds__(kThreads) void attn_fwd_short_kernel(FwdArgs a, int seqs_per_wg) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __bf16* Kl = reinterpret_cast<__bf16*>(smem);
+  __bf16* Vl = Kl + (int64_t)seqs_per_wg * a.Nk * D;
+  const int tid = threadIdx.x;
+  const int64_t bh0 = (int64_t)blockIdx.x * seqs_per_wg;
+  const int nseq = (int)min<int64_t>(seqs_per_wg, a.BH - bh0);
+
+  // Stage K and V of this workgroup's slices (contiguous) in LDS.
+  const int chunks = nseq * a.Nk * (D / 8);
+  const u32x4* Kg = reinterpret_cast<const u32x4*>(reinterpret_cast<const __bf16*>(a.k) + bh0 * a.Nk * D);
+  const u32x4* Vg = reinterpret_cast<const u32x4*>(reinterpret_cast<const __bf16*>(a.v) + bh0 * a.Nk * D);
+  for (int e = tid; e < chunks; e += kThreads) {
+    reinterpret_cast<u32x4*>(Kl)[e] = Kg[e];
+    reinterpret_cast<u32x4*>(Vl)[e] = Vg[e];
+  }
+  __syncthreads();
+
+  const int s = tid / a.Nq, i = tid % a.Nq;
+  if (s >= nseq) return;
+  const int64_t bh = bh0 + s;
+  const __bf16* qrow = reinterpret_cast<const __bf16*>(a.q) + (bh * a.Nq + i) * D;
+  float q[D];
+#pragma unroll
+  for (int c = 0; c < D; c += 8) {
+    const f32x8 x = __builtin_convertvector(*reinterpret_cast<const bf16x8*>(qrow + c), f32x8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[c + e] = x[e];
+  }
+  const __bf16* Ks = Kl + (int64_t)s * a.Nk * D;
+  const __bf16* Vs = Vl + (int64_t)s * a.Nk * D;
+  const int lim = a.causal ? min(i + a.diag, a.Nk - 1) : a.Nk - 1;   // last visible key of this row
+
+  float sc[kShortMax];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kShortMax; ++j) {
+    sc[j] = -INFINITY;
+    if (j <= lim) {
+      float dot = 0.0f;
+#pragma unroll
+      for (int c = 0; c < D; c += 8) {
+        const f32x8 kx = __builtin_convertvector(*reinterpret_cast<const bf16x8*>(Ks + j * D + c), f32x8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dot = __builtin_fmaf(q[c + e], kx[e], dot);
+      }
+      sc[j] = dot * a.scale_log2;
+      mx = fmaxf(mx, sc[j]);
+    }
+  }
+  float acc[D];
+#pragma unroll
+  for (int c = 0; c < D; ++c) acc[c] = 0.0f;
+  float l = 0.0f;
+  if (mx != -INFINITY) {
+#pragma unroll
+    for (int j = 0; j < kShortMax; ++j) {
+      if (j <= lim) {
+        const float p = __builtin_amdgcn_exp2f(sc[j] - mx);
+        l += p;
+#pragma unroll
+        for (int c = 0; c < D; c += 8) {
+          const f32x8 vx = __builtin_convertvector(*reinterpret_cast<const bf16x8*>(Vs + j * D + c), f32x8);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[c + e] = __builtin_fmaf(p, vx[e], acc[c + e]);
+        }
+      }
+    }
+  }
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  a.lse[bh * a.Nq + i] = l > 0.0f ? (mx + __builtin_amdgcn_logf(l)) * 0.69314718055994531f : -INFINITY;
+#pragma unroll
+  for (int c = 0; c < D; c += 4) {
+    const f32x4 y = {acc[c] * inv, acc[c + 1] * inv, acc[c + 2] * inv, acc[c + 3] * inv};
+    if (OF32)
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.o) + (bh * a.Nq + i) * D + c) = y;
+    else
+      *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(a.o) + (bh * a.Nq + i) * D + c) =
+          __builtin_convertvector(y, bf16x4);
+  }
+}
+
+template <int D, bool OF32>
+hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
+  constexpr int64_t kLdsBudget = 64 * 1024;
+  int64_t spw = kThreads / a.Nq;
+  const int64_t per_seq = 2LL * a.Nk * D * 2;   // K and V bytes of one slice
+  if (spw * per_seq > kLdsBudget) spw = kLdsBudget / per_seq;
+  if (spw < 1) return hipErrorInvalidValue;
+  const int64_t blocks = (a.BH + spw - 1) / spw;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((attn_fwd_short_kernel<D, OF32>), dim3((unsigned)blocks), dim3(kThreads),
+                     (size_t)(spw * per_seq), stream, a, (int)spw);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd_short(const FwdArgs& a, int d, int o_f32, hipStream_t stream) {
+  if (a.Nq > kShortMax || a.Nk > kShortMax || a.Nq < 1 || a.Nk < 1) return hipErrorInvalidValue;
+  switch (d) {
+    case 128: return o_f32 ? launch_d<128, true>(a, stream) : launch_d<128, false>(a, stream);
+    case 64: return o_f32 ? launch_d<64, true>(a, stream) : launch_d<64, false>(a, stream);
+    case 24: return o_f32 ? launch_d<24, true>(a, stream) : launch_d<24, false>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace ebattn

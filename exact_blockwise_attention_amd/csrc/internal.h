@@ -1,0 +1,52 @@
+// Internal declarations shared by the C-ABI layer (api.hip) and the kernel translation units.
+// Not installed; the public interface is include/ebattn.h.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ebattn {
+
+// Arguments of one attention-forward launch over B*H independent (batch, head) slices.
+// Layout: q [BH, Nq, d], k/v [BH, Nk, d], o [BH, Nq, d], lse [BH, Nq], all contiguous, d fastest.
+// Causal masking by global position reduces to "key j visible to query i iff j <= i + diag" (host computes
+// diag = floor((q_off - k_off) / pos_stride), clamped); non-causal launches ignore diag.
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t BH;
+  int Nq;
+  int Nk;
+  float scale_log2;   // softmax scale times log2(e): the kernels work in the exp2 domain
+  int causal;
+  int diag;
+};
+
+// bf16 operands on MFMA; d in {24, 64, 128}; o is bf16 (o_f32 = 0) or fp32 (o_f32 = 1).
+hipError_t launch_attn_fwd_bf16(const FwdArgs& a, int d, int o_f32, hipStream_t stream);
+// fp32 operands and output on the vector ALU (the fp32 correctness path); d in {24, 64, 128}.
+hipError_t launch_attn_fwd_f32(const FwdArgs& a, int d, hipStream_t stream);
+// Short sequences (Nq, Nk <= kShortMax), bf16 in, bf16/fp32 out, d in {24, 64, 128}: one lane per query row,
+// many (batch, head) slices per workgroup.
+constexpr int kShortMax = 16;
+hipError_t launch_attn_fwd_short(const FwdArgs& a, int d, int o_f32, hipStream_t stream);
+
+struct MergeArgs {
+  const void* o_a;
+  const float* lse_a;
+  const void* o_b;
+  const float* lse_b;
+  void* o;
+  float* lse;
+  int64_t rows;
+  int d;
+};
+// part_f32 / o_f32: 1 for fp32 tensors, 0 for bf16. d multiple of 4 (fp32 parts) or 8 (bf16 parts).
+hipError_t launch_lse_merge(const MergeArgs& a, int part_f32, int o_f32, hipStream_t stream);
+// Writes o = 0 (rows x d, bf16 or fp32) and lse = -inf (rows): the result for rows with no visible key.
+hipError_t launch_fill_empty(void* o, float* lse, int64_t rows, int d, int o_f32, hipStream_t stream);
+
+}  // namespace ebattn

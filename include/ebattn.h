@@ -1,0 +1,131 @@
+/* ebattn.h -- C ABI of the exact blockwise attention library for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes
+ * -------------------------
+ * Exact softmax attention, o_i = sum_j softmax_j(scale * q_i . k_j) v_j over the keys j visible to query i, and
+ * its per-row natural-log normaliser lse_i = log sum_j exp(scale * q_i . k_j):
+ *   - the three-step definition of "深度学习注意力机制优化与FlashAttention实践" §2.1 (scores, softmax over keys,
+ *     weighted sum of V), with the scale an explicit argument;
+ *   - computed blockwise with an online softmax as in §4.2 of the same page (running maximum and running sum
+ *     per query row, output rescaled whenever the maximum grows), which reaches the same result up to
+ *     rounding ("架构层解决方案 - Sparse Attention与Ring Attention", Ring Attention / 核心创新);
+ *   - partial results over disjoint key sets combine exactly with the log-sum-exp merge of
+ *     "分布式注意力机制突破：长序列处理的全景技术架构与实践指南" §3.4 (and §2.2 stage 3, pairwise form with the
+ *     sign of its exponent corrected);
+ *   - ring_local is one device's share of Ring Attention ("Mosaic多轴注意力分片：突破Transformer长序列处理瓶颈"
+ *     §3.2): a resident query shard attended against a sequence of key/value blocks, merged as they come,
+ *     ending with the complete output of that shard.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *   Layout    q, k, v, o are contiguous [B, H, N, d] (row-major, d fastest; "BHSD"); lse is fp32 [B, H, Nq].
+ *             lse is the natural log of the sum of exp(scale * q.k) over the visible keys (no bias).
+ *   Pointers  q, k, v, o, lse, the merge operands and the workspace are DEVICE pointers owned by the caller;
+ *             the library never frees or keeps them. Tensor pointers must be 16-byte aligned, lse pointers
+ *             4-byte aligned. `stream` is a hipStream_t (NULL = the default stream).
+ *   Masks     causal = 0: every key is visible. causal = 1: the mask is by GLOBAL POSITION. Local query row i
+ *             sits at position q_off + i*pos_stride, local key j at k_off + j*pos_stride, and key j is visible
+ *             to query i iff its position is <= the query's (inclusive diagonal, "深度学习注意力机制优化与
+ *             FlashAttention实践" §5.1). pos_stride = 1 for contiguous shards; striping a sequence over W
+ *             devices (token t on device t mod W, "注意力机制演进" timeline, Striped Attention) uses
+ *             pos_stride = W, q_off = the query stripe, k_off = the key stripe.
+ *   Empty rows A query row with no visible key gets o = 0 and lse = -inf (no epsilon anywhere); the merge
+ *             gives such a part zero weight.
+ *   Dtypes    ATTN_BF16 inputs run on bf16 MFMA with fp32 accumulation and fp32 softmax statistics
+ *             ("深度学习注意力机制优化与FlashAttention实践" §5.1 advises fp32 for the statistics); the softmax
+ *             weights P are rounded to bf16 before the P.V product. ATTN_F32 inputs run in fp32 throughout.
+ *   Asynchrony Every call only enqueues work on `stream`; nothing synchronises the device.
+ *   Errors    Return ATTN_OK (0) or a negative code. Argument errors are detected before anything is
+ *             launched; attn_last_error() then holds a message (thread-local). Launch failures return
+ *             ATTN_EHIP with the HIP error string. Nothing throws across this boundary. On error the contents
+ *             of the outputs are unspecified.
+ */
+#ifndef EBATTN_H
+#define EBATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_OK 0
+#define ATTN_EINVAL (-1)        /* bad argument: null pointer, negative size, bad flag, misalignment, overlap */
+#define ATTN_EUNSUPPORTED (-2)  /* well-formed but not implemented: head dim, dtype combination */
+#define ATTN_EHIP (-3)          /* the HIP runtime reported an error while launching */
+#define ATTN_EWORKSPACE (-4)    /* ring_local: workspace missing or smaller than ring_local_workspace_bytes() */
+
+#define ATTN_F32 0
+#define ATTN_BF16 1
+
+/* Largest sequence length (Nq, Nk) accepted by every entry point. */
+#define ATTN_MAX_SEQ (1 << 28)
+
+/* attn_fwd -- exact attention of q [B,H,Nq,d] against k, v [B,H,Nk,d]; writes o [B,H,Nq,d] and lse [B,H,Nq].
+ *   scale       softmax scale applied to q.k (workloads use 1/sqrt(d)); must be finite and > 0.
+ *   causal      0 or 1, see "Masks"; q_off, k_off, pos_stride (>= 1) give the global positions.
+ *   in_dtype    ATTN_BF16 (d in {24, 64, 128}) or ATTN_F32 (d in {24, 64, 128}).
+ *   o_dtype     ATTN_BF16 or ATTN_F32 for bf16 inputs; ATTN_F32 for fp32 inputs.
+ *   Sizes       B, H, Nq, Nk >= 0 (zero-sized calls are no-ops, except Nk = 0, which writes (0, -inf) rows);
+ *               Nq, Nk <= ATTN_MAX_SEQ. k and v may be NULL when Nk = 0.
+ *   Overlap     o and lse must not overlap q, k, v or each other.
+ *   Sequences of at most 16 queries and 16 keys take a one-lane-per-row path (fp32 weights, no bf16 P). */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int Nq, int Nk, int d, float scale, int causal,
+             int64_t q_off, int64_t k_off, int pos_stride, int in_dtype, int o_dtype, void* stream);
+
+/* attn_lse_merge -- merges two partial results over disjoint key sets of the same query rows:
+ *   lse = log(exp(lse_a) + exp(lse_b)),  o = exp(lse_a - lse) * o_a + exp(lse_b - lse) * o_b.
+ *   Operands are `rows` rows of d values (any [.., rows, d] contiguous layout; for attention rows = B*H*Nq).
+ *   part_dtype  dtype of o_a and o_b (ATTN_F32: d a multiple of 4, <= 256; ATTN_BF16: multiple of 8, <= 512).
+ *   o_dtype     dtype of o. lse_* and lse are fp32.
+ *   In place    o may be exactly o_a or o_b when o_dtype == part_dtype, and lse may be exactly lse_a or lse_b;
+ *               any other overlap is ATTN_EINVAL.
+ *   Empty       a part with lse = -inf weighs zero; two empty parts give (0, -inf). rows = 0 is a no-op. */
+int attn_lse_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
+                   void* o, float* lse, int64_t rows, int d, int part_dtype, int o_dtype, void* stream);
+
+/* One key/value block of a ring: k, v [B,H,Nk,d] (same B, H, d and dtype as the query shard), and the global
+ * position of its first key (positions advance by pos_stride per key, as for attn_fwd). */
+typedef struct {
+  const void* k;
+  const void* v;
+  int Nk;
+  int64_t k_off;
+} attn_kv_block;
+
+/* ring_local -- one device's share of Ring Attention: q_shard [B,H,Nq,d] against kv_blocks[0..n_blocks-1],
+ * processed in the given order (the order the blocks would arrive around the ring). Blocks that hide every
+ * key from every query row (causal) are skipped without a launch. The first live block's attention goes to
+ * the fp32 accumulator in the workspace, every later block's to a second fp32 partial that is merged into the
+ * accumulator; the last merge writes o (o_dtype) and lse. A single live block writes o and lse directly; no
+ * live block writes (0, -inf) rows. The result equals attention over the union of the blocks.
+ *   workspace   device buffer of at least ring_local_workspace_bytes(B, H, Nq, d) bytes, 256-byte aligned,
+ *               not overlapping anything else; may be NULL only if at most one block is live.
+ *   Other arguments as attn_fwd. */
+int ring_local(const void* q_shard, const attn_kv_block* kv_blocks, int n_blocks, void* o, float* lse,
+               int B, int H, int Nq, int d, float scale, int causal, int64_t q_off, int pos_stride,
+               int in_dtype, int o_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace ring_local needs: two fp32 (o, lse) buffers of B*H*Nq rows, each 256-byte aligned.
+ * Returns 0 for negative sizes. */
+size_t ring_local_workspace_bytes(int B, int H, int Nq, int d);
+
+/* ring_local_plan -- host-only classification of each block, exactly as ring_local decides it (no device
+ * work). kinds[i] = 0: every key hidden from every row (skipped); 1: every key visible to every row;
+ * 2: partly visible. Returns the number of live (kind != 0) blocks, or a negative error code. */
+int ring_local_plan(const attn_kv_block* kv_blocks, int n_blocks, int Nq, int causal, int64_t q_off,
+                    int pos_stride, int* kinds);
+
+/* Message describing the last error returned on the calling thread ("" if none). Owned by the library. */
+const char* attn_last_error(void);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EBATTN_H */

@@ -1,0 +1,178 @@
+"""The C ABI on the CPU: the library loads, exports every declared function, validates its arguments before
+touching the device, and plans ring blocks on the host exactly as the oracle's mask says."""
+import ctypes
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+
+eb = pytest.importorskip("exact_blockwise_attention_amd")
+lib = eb.lib
+A = 1 << 20          # fake, well-aligned "device" addresses: validation must reject before any use
+B16 = 1 << 24
+
+
+def test_every_declared_symbol_is_exported():
+    names = eb.declared_symbols()
+    assert set(names) >= {"attn_fwd", "attn_lse_merge", "ring_local", "ring_local_workspace_bytes",
+                          "ring_local_plan", "attn_last_error", "attn_version"}
+    out = subprocess.run(["nm", "-D", "--defined-only", eb.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for n in names:
+        assert n in exported, n
+        assert hasattr(lib, n)
+    assert lib.attn_version() == 100
+
+
+def test_workspace_bytes():
+    def a256(x):
+        return (x + 255) // 256 * 256
+    for B, H, Nq, d in [(1, 32, 32768, 128), (1, 1, 256, 64), (3, 5, 7, 24), (0, 1, 1, 128)]:
+        rows = B * H * Nq
+        assert eb.ring_local_workspace_bytes(B, H, Nq, d) == 2 * (a256(rows * d * 4) + a256(rows * 4))
+    assert eb.ring_local_workspace_bytes(-1, 1, 1, 1) == 0
+
+
+def fwd(**kw):
+    args = dict(q=A, k=A + B16, v=A + 2 * B16, o=A + 3 * B16, lse=A + 4 * B16, B=1, H=2, Nq=64, Nk=64, d=128,
+                scale=0.125, causal=1, q_off=0, k_off=0, stride=1, it=eb.ATTN_BF16, ot=eb.ATTN_BF16, stream=None)
+    args.update(kw)
+    return lib.attn_fwd(args["q"], args["k"], args["v"], args["o"], args["lse"], args["B"], args["H"], args["Nq"],
+                        args["Nk"], args["d"], args["scale"], args["causal"], args["q_off"], args["k_off"],
+                        args["stride"], args["it"], args["ot"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), eb.ATTN_EINVAL),
+    (dict(o=None), eb.ATTN_EINVAL),
+    (dict(lse=None), eb.ATTN_EINVAL),
+    (dict(k=None), eb.ATTN_EINVAL),
+    (dict(B=-1), eb.ATTN_EINVAL),
+    (dict(Nq=-3), eb.ATTN_EINVAL),
+    (dict(Nk=-3), eb.ATTN_EINVAL),
+    (dict(Nq=(1 << 28) + 1), eb.ATTN_EINVAL),
+    (dict(causal=2), eb.ATTN_EINVAL),
+    (dict(stride=0), eb.ATTN_EINVAL),
+    (dict(scale=0.0), eb.ATTN_EINVAL),
+    (dict(scale=-1.0), eb.ATTN_EINVAL),
+    (dict(scale=float("nan")), eb.ATTN_EINVAL),
+    (dict(scale=float("inf")), eb.ATTN_EINVAL),
+    (dict(it=7), eb.ATTN_EINVAL),
+    (dict(d=32), eb.ATTN_EUNSUPPORTED),
+    (dict(d=256), eb.ATTN_EUNSUPPORTED),
+    (dict(it=eb.ATTN_F32, ot=eb.ATTN_BF16), eb.ATTN_EUNSUPPORTED),
+    (dict(q=A + 8), eb.ATTN_EINVAL),                 # misaligned
+    (dict(v=A + 2 * B16 + 4), eb.ATTN_EINVAL),
+    (dict(lse=A + 4 * B16 + 2), eb.ATTN_EINVAL),
+    (dict(o=A + 16), eb.ATTN_EINVAL),                # o overlaps q
+    (dict(lse=A + 3 * B16 + 64), eb.ATTN_EINVAL),    # lse overlaps o
+    (dict(o=A + B16 + 256), eb.ATTN_EINVAL),         # o overlaps k
+    (dict(q_off=(1 << 62) + 1), eb.ATTN_EINVAL),
+    (dict(k_off=-(1 << 62) - 1), eb.ATTN_EINVAL),
+])
+def test_attn_fwd_validation(kw, code):
+    assert fwd(**kw) == code
+    assert eb.last_error() != ""
+
+
+def test_zero_sized_calls_are_noops():
+    assert fwd(B=0) == eb.ATTN_OK
+    assert fwd(H=0, q=None, o=None, lse=None) == eb.ATTN_OK
+    assert fwd(Nq=0) == eb.ATTN_OK
+    assert eb.last_error() == ""
+
+
+def merge(**kw):
+    args = dict(oa=A, la=A + B16, ob=A + 2 * B16, lb=A + 3 * B16, o=A + 4 * B16, l=A + 5 * B16, rows=100, d=128,
+                pt=eb.ATTN_F32, ot=eb.ATTN_F32)
+    args.update(kw)
+    return lib.attn_lse_merge(args["oa"], args["la"], args["ob"], args["lb"], args["o"], args["l"], args["rows"],
+                              args["d"], args["pt"], args["ot"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(rows=-1), eb.ATTN_EINVAL),
+    (dict(d=0), eb.ATTN_EINVAL),
+    (dict(d=6), eb.ATTN_EUNSUPPORTED),
+    (dict(d=12, pt=eb.ATTN_BF16), eb.ATTN_EUNSUPPORTED),
+    (dict(d=260), eb.ATTN_EUNSUPPORTED),
+    (dict(pt=3), eb.ATTN_EINVAL),
+    (dict(oa=None), eb.ATTN_EINVAL),
+    (dict(o=A + 64), eb.ATTN_EINVAL),                  # partial overlap with o_a
+    (dict(o=A, ot=eb.ATTN_BF16), eb.ATTN_EINVAL),     # in place needs the same dtype
+    (dict(o=A, ob=A), eb.ATTN_EINVAL),                # all three the same buffer
+    (dict(l=A + B16 + 4), eb.ATTN_EINVAL),            # partial overlap with lse_a
+    (dict(l=A + 4 * B16 + 128), eb.ATTN_EINVAL),      # lse inside o
+    (dict(o=A + 8), eb.ATTN_EINVAL),                  # misaligned
+])
+def test_merge_validation(kw, code):
+    assert merge(**kw) == code
+
+
+def test_merge_zero_rows_is_noop():
+    assert merge(rows=0) == eb.ATTN_OK
+
+
+def _blocks(spec):
+    arr = (eb.KVBlock * max(1, len(spec)))()
+    for i, (nk, ko) in enumerate(spec):
+        arr[i] = eb.KVBlock(A + (2 * i + 8) * B16, A + (2 * i + 9) * B16, nk, ko)
+    return arr
+
+
+def ring(spec, ws=A + 40 * B16, ws_bytes=None, **kw):
+    args = dict(q=A, o=A + B16, l=A + 2 * B16, B=1, H=2, Nq=64, d=64, scale=0.125, causal=1, q_off=128, stride=1,
+                it=eb.ATTN_BF16, ot=eb.ATTN_BF16)
+    args.update(kw)
+    if ws_bytes is None:
+        ws_bytes = eb.ring_local_workspace_bytes(args["B"], args["H"], args["Nq"], args["d"])
+    arr = _blocks(spec)
+    return lib.ring_local(args["q"], arr, len(spec), args["o"], args["l"], args["B"], args["H"], args["Nq"], args["d"],
+                          args["scale"], args["causal"], args["q_off"], args["stride"], args["it"], args["ot"], ws,
+                          ws_bytes, None)
+
+
+def test_ring_local_validation():
+    spec = [(64, 0), (64, 64), (64, 128)]
+    assert ring(spec, ws=None) == eb.ATTN_EWORKSPACE
+    assert ring(spec, ws_bytes=100) == eb.ATTN_EWORKSPACE
+    assert ring(spec, ws=A + 40 * B16 + 16) == eb.ATTN_EINVAL           # misaligned workspace
+    assert ring(spec, ws=A + 8 * B16 + 256) == eb.ATTN_EINVAL           # workspace inside block 0's k
+    assert ring([(64, 0), (-1, 5)]) == eb.ATTN_EINVAL
+    assert ring(spec, stride=0) == eb.ATTN_EINVAL
+    assert ring(spec, d=48) == eb.ATTN_EUNSUPPORTED
+    assert "workspace" in eb.last_error() or eb.last_error() != ""
+    assert ring([], Nq=0) == eb.ATTN_OK
+
+
+def _brute_kind(nq, nk, causal, q_off, k_off, stride):
+    vis = oracle.visible(nq, nk, causal, q_off, k_off, stride)
+    if nk == 0 or not vis.any():
+        return 0
+    return 1 if vis.all() else 2
+
+
+@pytest.mark.parametrize("causal", [0, 1])
+def test_ring_plan_matches_oracle_mask(causal):
+    rng = np.random.default_rng(3)
+    for _ in range(200):
+        nq = int(rng.integers(1, 40))
+        stride = int(rng.choice([1, 2, 4]))
+        q_off = int(rng.integers(-50, 50))
+        spec = [(int(rng.integers(0, 40)), int(rng.integers(-80, 80))) for _ in range(int(rng.integers(1, 5)))]
+        live, kinds = eb.ring_local_plan(nq, spec, causal=causal, q_off=q_off, pos_stride=stride)
+        want = [_brute_kind(nq, nk, causal, q_off, ko, stride) for nk, ko in spec]
+        assert kinds == want
+        assert live == sum(k != 0 for k in want)
+
+
+def test_ring_plan_named_workloads():
+    n = 32768
+    live, kinds = eb.ring_local_plan(n, [(n, 0), (n, n), (n, 2 * n), (n, 3 * n)], causal=True, q_off=2 * n)
+    assert (live, kinds) == (3, [1, 1, 2, 0])
+    for r in range(4):
+        live, kinds = eb.ring_local_plan(16384, [(16384, s) for s in range(4)], causal=True, q_off=r, pos_stride=4)
+        assert (live, kinds) == (4, [2, 2, 2, 2])
+    assert eb.ring_local_plan(256, [(64, 64 * i) for i in range(4)], causal=False) == (4, [1, 1, 1, 1])
