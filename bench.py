@@ -1,0 +1,271 @@
+"""Benchmark of the exact blockwise attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu] [--copy-probe BYTES]
+
+A step is one attention forward (scores, causal mask by position, online softmax, P.V, epilogue) over the
+causal self-attention workload B=4, H=32, N=8192, d=128, bf16 in / bf16 out with fp32 lse, inputs iid N(0,1)
+seeded and already resident in HBM. The printed JSON line reports:
+  value      TFLOP/s = 4*d*(visible query/key pairs) per step / wall time per step (HIP events on the launch
+             stream around the K timed steps, bracketed by device synchronisation);
+  roofline   the attention kernel against the bf16 dense MFMA peak; `traffic` is the measured HBM bytes per
+             launch from the committed rocprofv3 counter summary when it was taken on the current kernel
+             source, else null;
+  cpu_baseline  the float64 oracle timed on this host on a bounded row sample of the same workload;
+  extra      secondary measurements: the LSE merge at the ring-share shape (HBM-bound) and the ring-share /
+             striped workloads end to end.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s + % bf16 MFMA peak (causal, N=8K..128K, 1 GPU)"
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk/CU
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+KERNEL_SOURCE = os.path.join(ROOT, "exact_blockwise_attention_amd", "csrc", "attn_fwd_mfma.hip")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "attn_fwd_causal_8k_hbm_traffic.txt")
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic():
+    """HBM bytes per launch from the committed counter summary, if it matches the current kernel source."""
+    if not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    text = open(TRAFFIC_SUMMARY, encoding="utf-8").read()
+    h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not h or not b or h.group(1) != kernel_hash():
+        return None
+    return float(b.group(1))
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def upload_bf16(bits, torch, dev):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def time_region(torch, fn, steps, warmup):
+    """Runs fn warmup times, then times `steps` calls with events on the current stream; returns ms/step."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(steps):
+        fn()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def cpu_baseline(cfg, q_bits, k_bits, v_bits, budget_s=12.0):
+    """The oracle on a bounded row sample of the workload (one head, rows spread over the sequence)."""
+    import oracle
+    from workloads import accounting as acc
+    from workloads import bf16_bits_to_f64
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    q = bf16_bits_to_f64(q_bits[:1, :1])
+    k = bf16_bits_to_f64(k_bits[:1, :1])
+    v = bf16_bits_to_f64(v_bits[:1, :1])
+    rng = np.random.default_rng(0)
+    rows_done, flops, elapsed = 0, 0.0, 0.0
+    chunk = 256
+    t0 = time.perf_counter()
+    while elapsed < budget_s and rows_done < cfg.Nq:
+        rows = np.sort(rng.choice(cfg.Nq, size=chunk, replace=False))
+        oracle.attention(q, k, v, cfg.scale, causal=cfg.causal, rows=rows)
+        vis = np.minimum(rows + 1, cfg.Nq) if cfg.causal else np.full(rows.size, cfg.Nq)
+        flops += acc.attention_flops(int(vis.sum()), cfg.d)
+        rows_done += chunk
+        elapsed = time.perf_counter() - t0
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{rows_done} random query rows of head (0,0) of {cfg.key} (float64 numpy oracle, "
+                      f"{elapsed:.1f} s), rate = 4*d*visible pairs of the sample / time"}
+
+
+def bench_extra(torch, eb, dev, steps):
+    """Merge bandwidth at the ring-share shape, and the ring-share / striped workloads end to end."""
+    from workloads import CONFIGS, normal_bf16_bits
+    from workloads import accounting as acc
+    out = {}
+    # LSE merge, fp32 partials in place: 32*32768 rows x d=128 (1.62 GB moved per launch)
+    rows, d = 32 * 32768, 128
+    g = torch.Generator(device=dev)
+    g.manual_seed(3)
+    oa = torch.randn((rows, d), device=dev, generator=g)
+    ob = torch.randn((rows, d), device=dev, generator=g)
+    la = torch.randn((rows,), device=dev, generator=g)
+    lb = torch.randn((rows,), device=dev, generator=g)
+    ms = time_region(torch, lambda: eb.attn_lse_merge(oa, la, ob, lb, out=oa, lse_out=la), max(steps, 10), 3)
+    nbytes = acc.merge_bytes(rows, d, 4, 4)
+    out["lse_merge_f32_inplace_1M_rows_d128"] = {"ms": ms, "GB/s": nbytes / ms / 1e6,
+                                                 "frac_hbm_peak": nbytes / ms / 1e6 / PEAK_HBM_GBS,
+                                                 "bytes_per_launch": nbytes}
+    del oa, ob, la, lb
+    # ring share, rank 2 of 4, global N = 131072
+    c3 = CONFIGS["ring_rank2of4_128k"]
+    n = c3.Nq
+    t0 = time.perf_counter()
+    Q = normal_bf16_bits(c3.seed, "q", (c3.B, c3.H, c3.global_N, c3.d))
+    qd = upload_bf16(Q[:, :, c3.q_off:c3.q_off + n], torch, dev)
+    del Q
+    K = normal_bf16_bits(c3.seed, "k", (c3.B, c3.H, c3.global_N, c3.d))
+    kd = [upload_bf16(K[:, :, s * n:(s + 1) * n], torch, dev) for s in range(4)]
+    del K
+    V = normal_bf16_bits(c3.seed, "v", (c3.B, c3.H, c3.global_N, c3.d))
+    vd = [upload_bf16(V[:, :, s * n:(s + 1) * n], torch, dev) for s in range(4)]
+    del V
+    log(f"[bench] ring-share inputs ready in {time.perf_counter() - t0:.1f} s")
+    order = [2, 1, 0, 3]
+    blocks = [(kd[s], vd[s], s * n) for s in order]
+    ws = torch.empty(eb.ring_local_workspace_bytes(c3.B, c3.H, n, c3.d), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(qd)
+    lse = torch.empty((c3.B, c3.H, n), dtype=torch.float32, device=dev)
+    ms = time_region(torch, lambda: eb.ring_local(qd, blocks, causal=True, q_off=c3.q_off, out=o, lse=lse,
+                                                  workspace=ws), max(2, steps // 4), 1)
+    fl = acc.attention_flops(acc.config_pairs(c3), c3.d)
+    out["ring_local_rank2of4_128k"] = {"ms": ms, "TFLOP/s": fl / ms / 1e9, "frac_mfma_peak": fl / ms / 1e9 / PEAK_BF16_TFLOPS}
+    del qd, kd, vd, blocks, ws, o, lse
+    torch.cuda.empty_cache()
+    # striped: all four query stripes of N = 65536, H = 16
+    per_rank = {}
+    c4 = CONFIGS["striped_r0_64k"]
+    Q = normal_bf16_bits(c4.seed, "q", (c4.B, c4.H, c4.global_N, c4.d))
+    K = normal_bf16_bits(c4.seed, "k", (c4.B, c4.H, c4.global_N, c4.d))
+    V = normal_bf16_bits(c4.seed, "v", (c4.B, c4.H, c4.global_N, c4.d))
+    kd = [upload_bf16(K[:, :, s::4], torch, dev) for s in range(4)]
+    vd = [upload_bf16(V[:, :, s::4], torch, dev) for s in range(4)]
+    ws = torch.empty(eb.ring_local_workspace_bytes(c4.B, c4.H, c4.Nq, c4.d), dtype=torch.uint8, device=dev)
+    for r in range(4):
+        cr = CONFIGS[f"striped_r{r}_64k"]
+        qd = upload_bf16(Q[:, :, r::4], torch, dev)
+        blocks = [(kd[s], vd[s], s) for s in [(r - i) % 4 for i in range(4)]]
+        o = torch.empty_like(qd)
+        lse = torch.empty((cr.B, cr.H, cr.Nq), dtype=torch.float32, device=dev)
+        ms = time_region(torch, lambda: eb.ring_local(qd, blocks, causal=True, q_off=r, pos_stride=4, out=o,
+                                                      lse=lse, workspace=ws), max(2, steps // 2), 1)
+        fl = acc.attention_flops(acc.config_pairs(cr), cr.d)
+        per_rank[f"r{r}"] = {"ms": ms, "TFLOP/s": fl / ms / 1e9, "frac_mfma_peak": fl / ms / 1e9 / PEAK_BF16_TFLOPS}
+    out["striped_64k_ring_local"] = per_rank
+    return out
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-extra", action="store_true", help="skip the merge / ring-share / striped measurements")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="also run one plain device copy of this many bytes (counter calibration)")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this build has no "
+              "multi-GPU path)", file=sys.stderr)
+        return 2
+
+    import torch
+    import exact_blockwise_attention_amd as eb
+    from workloads import CONFIGS, normal_bf16_bits
+    from workloads import accounting as acc
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = CONFIGS["causal_8k"]
+    t0 = time.perf_counter()
+    q_bits = normal_bf16_bits(cfg.seed, "q", (cfg.B, cfg.H, cfg.Nq, cfg.d))
+    k_bits = normal_bf16_bits(cfg.seed, "k", (cfg.B, cfg.H, cfg.Nk_total, cfg.d))
+    v_bits = normal_bf16_bits(cfg.seed, "v", (cfg.B, cfg.H, cfg.Nk_total, cfg.d))
+    q, k, v = (upload_bf16(x, torch, dev) for x in (q_bits, k_bits, v_bits))
+    o = torch.empty_like(q)
+    lse = torch.empty((cfg.B, cfg.H, cfg.Nq), dtype=torch.float32, device=dev)
+    log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s")
+
+    if args.copy_probe > 0:
+        src = torch.empty(args.copy_probe // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: {src.numel() * 4} bytes read, {dst.numel() * 4} bytes written")
+        del src, dst
+
+    def step():
+        eb.attn_fwd(q, k, v, scale=cfg.scale, causal=True, out=o, lse=lse)
+
+    # barrier + synchronise on both sides of the timed region (one process: the device sync is the barrier)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - w0) * 1e3 / args.steps
+    ev_ms = e0.elapsed_time(e1) / args.steps
+    log(f"[bench] attn_fwd: {ev_ms:.3f} ms/step on events, {wall_ms:.3f} ms/step wall")
+
+    flops = acc.attention_flops(acc.config_pairs(cfg), cfg.d)
+    tflops = flops / ev_ms / 1e9
+    traffic = stored_traffic()
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ev_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded iid N(0,1) rounded to bf16, resident in HBM",
+        "config": {"workload": "causal self-attention B=4 H=32 N=8192 d=128, bf16 in/out, fp32 lse",
+                   "B": cfg.B, "H": cfg.H, "N": cfg.Nq, "d": cfg.d, "causal": True,
+                   "flop_per_step": flops, "visible_pairs": acc.config_pairs(cfg)},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "attn_fwd_kernel<128,bf16 out>", "kernel_source_sha256_16": kernel_hash()},
+    }
+    if not args.no_extra:
+        try:
+            result["extra"] = bench_extra(torch, eb, dev, args.steps)
+        except Exception as exc:  # the headline line is printed regardless
+            result["extra"] = {"error": repr(exc)}
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(cfg, q_bits, k_bits, v_bits)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
