@@ -47,6 +47,14 @@ class KVBlock(ctypes.Structure):
 
 
 def _load() -> ctypes.CDLL:
+    # PyTorch-ROCm ships its own HIP runtime whose soname (libamdhip64.so.7) matches this library's dependency.
+    # Loading torch first lets the dynamic linker satisfy that dependency with torch's runtime, so the process
+    # has one HIP runtime and torch's device memory and streams are valid here. Loading this library first
+    # would bring in a second runtime next to torch's.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python -m exact_blockwise_attention_amd.build` "
                           "(there is no fallback implementation)")

@@ -23,6 +23,8 @@
 //     (within each 16-lane group, lane i receives column i of a 4-row x 16-column block);
 //   * K rows and V rows are XOR-swizzled per 16-byte chunk so that both the operand reads and the LDS writes
 //     of the copy spread over all banks;
+//   * O is normalised by the sum of the same bf16-rounded weights that enter P.V (packed bf16 dot with (1,1));
+//     the log-sum-exp uses the sum of the fp32 weights;
 //   * the reference maximum is only moved when a row's new maximum exceeds it by more than 8 (log2 units), so
 //     most tiles skip the rescale of the accumulator; the weights stay below 2^8 and the result is unchanged
 //     (the final normalisation uses the same reference).
@@ -35,6 +37,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -117,7 +120,7 @@ __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0
 // (compile-time, so they fold into the instructions' offset fields). `partial` tiles apply the mask.
 template <int D, int KB, int VB>
 __device__ __forceinline__ void compute_tile(const char* smem, const bf16x8 (&qf)[Geom<D>::KSTEPS],
-                                             f32x16 (&acc)[Geom<D>::CT], float& m_ref, float& l_run, bool partial,
+                                             f32x16 (&acc)[Geom<D>::CT], float& m_ref, float& l_run, float& lq_run, bool partial,
                                              int lim, float scale_log2, int k_row, int k_xor, int hi,
                                              const int (&v_addr)[Geom<D>::CT]) {
   using G = Geom<D>;
@@ -168,6 +171,19 @@ __device__ __forceinline__ void compute_tile(const char* smem, const bf16x8 (&qf
   pb[1] = __builtin_convertvector(__builtin_shufflevector(s0, s0, 8, 9, 10, 11, 12, 13, 14, 15), bf16x8);
   pb[2] = __builtin_convertvector(__builtin_shufflevector(s1, s1, 0, 1, 2, 3, 4, 5, 6, 7), bf16x8);
   pb[3] = __builtin_convertvector(__builtin_shufflevector(s1, s1, 8, 9, 10, 11, 12, 13, 14, 15), bf16x8);
+  // Two row sums: l_run over the fp32 weights gives the log-sum-exp; lq_run over the bf16-rounded weights that
+  // enter P.V (one packed dot with (1, 1) per pair) normalises O, so numerator and denominator use the same
+  // weights and a constant V comes back exactly.
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float psum0 = 0.0f, psum1 = 0.0f;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    psum0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[kk], pb[kk], 0, 1), ones, psum0, false);
+    psum1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[kk], pb[kk], 2, 3), ones, psum1, false);
+    psum0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[kk], pb[kk], 4, 5), ones, psum0, false);
+    psum1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[kk], pb[kk], 6, 7), ones, psum1, false);
+  }
+  lq_run = __builtin_fmaf(alpha, lq_run, psum0 + psum1);
   // V^T operand via two transpose reads: slots 0-3 from key rows +0..3, slots 4-7 from +4..7 of the 8-key group.
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
@@ -242,7 +258,7 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
   f32x16 acc[G::CT];
 #pragma unroll
   for (int ct = 0; ct < G::CT; ++ct) acc[ct] = f32x16{};
-  float m_ref = -INFINITY, l_run = 0.0f;
+  float m_ref = -INFINITY, l_run = 0.0f, lq_run = 0.0f;
   const int qi = q0 + wave * 32 + l32;     // this lane's query row
   const int row_lim = (a.causal ? min(qi + a.diag, a.Nk - 1) : a.Nk - 1) - 8 * hi;
 
@@ -257,7 +273,7 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
     __syncthreads();
     if (t + 1 < ntiles) issue_tile_copy<D>(K, V, (t + 1) * kBN, a.Nk, smem + KN, smem + VN, wave, lane);
     if (t * kBN < wave_kend)
-      compute_tile<D, KB, VB>(smem, qf, acc, m_ref, l_run, t >= nfull, row_lim - t * kBN, a.scale_log2, k_row,
+      compute_tile<D, KB, VB>(smem, qf, acc, m_ref, l_run, lq_run, t >= nfull, row_lim - t * kBN, a.scale_log2, k_row,
                               k_xor, hi, v_addr);
   };
   for (int t = 0; t < ntiles; t += 2) {
@@ -267,7 +283,8 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
 
   // Epilogue: O = acc / l, lse = ln2 * (m + log2 l); a row with no visible key gives (0, -inf).
   const float l_tot = pair_sum(l_run);
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  const float lq_tot = pair_sum(lq_run);
+  const float inv = lq_tot > 0.0f ? 1.0f / lq_tot : 0.0f;
   if (hi == 0 && qi < a.Nq)
     a.lse[bh * (int64_t)a.Nq + qi] =
         l_tot > 0.0f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f : -INFINITY;
