@@ -7,27 +7,27 @@
 // FlashAttention实践" §5.1) arrives here as a diagonal offset: key j is visible to query i iff j <= i + diag.
 // Only O and the per-row log-sum-exp are written to HBM ("注意力机制演进", section FlashAttention).
 //
-// Work decomposition (one workgroup = 4 waves = 128 query rows of one (batch, head)):
-//   * each wave owns 32 query rows; its Q fragment stays in VGPRs for the whole key loop;
-//   * 64-key K and V tiles are copied HBM -> LDS by the buffer unit itself (buffer_load ... lds, 16 bytes per
-//     lane, out-of-range rows read as zero), double-buffered so that tile t+1 streams in while tile t is
-//     consumed; one workgroup barrier per tile;
-//   * the wave computes S^T = K . Q^T (32 keys x 32 queries per MFMA 32x32x16). In that orientation one lane
-//     owns one query row (the MFMA output column): the row maximum and sum are in-lane reductions plus one
-//     exchange with the partner lane (lane ^ 32), and the rescale factor is a per-lane scalar;
+// Per wave (32 query rows, Q fragment held in VGPRs for the whole key loop):
+//   * S^T = K . Q^T, 32 keys x 32 queries per MFMA 32x32x16. In that orientation one lane owns one query row
+//     (the MFMA output column): the row maximum and sum are in-lane reductions plus one exchange with the
+//     partner lane (lane ^ 32), and the rescale factor is a per-lane scalar;
 //   * the keys of each 32-key chunk sit in LDS with bits 2 and 3 of their index swapped. Read back in natural
 //     order as the MFMA A operand, this leaves lane l's 16 output registers holding, in order, 8 consecutive
 //     keys of each 16-key half -- the B-operand layout of the next product O^T = V^T . P^T, so P goes from the
 //     S accumulator to the P.V MFMA without leaving the registers;
 //   * V stays row-major in LDS; the V^T operand is gathered with the LDS transpose read ds_read_b64_tr_b16
 //     (within each 16-lane group, lane i receives column i of a 4-row x 16-column block);
-//   * K rows and V rows are XOR-swizzled per 16-byte chunk so that both the operand reads and the LDS writes
-//     of the copy spread over all banks;
 //   * O is normalised by the sum of the same bf16-rounded weights that enter P.V (packed bf16 dot with (1,1));
 //     the log-sum-exp uses the sum of the fp32 weights;
-//   * the reference maximum is only moved when a row's new maximum exceeds it by more than 8 (log2 units), so
-//     most tiles skip the rescale of the accumulator; the weights stay below 2^8 and the result is unchanged
-//     (the final normalisation uses the same reference).
+//   * the reference maximum only moves when a row's new maximum exceeds it by more than 8 (log2 units), so most
+//     tiles skip the rescale of the accumulator; the weights stay below 2^8 and the result is unchanged (the
+//     final normalisation uses the same reference).
+// Per workgroup:
+//   * 64-key K and V tiles are copied HBM -> LDS by the buffer unit itself (buffer_load ... lds, 16 bytes per
+//     lane, rows past Nk read as zero), double-buffered in four separately named LDS arrays; K rows and V rows
+//     are XOR-swizzled per 16-byte chunk so that the operand reads spread over all 64 LDS banks;
+//   * 4 waves = 128 query rows per workgroup, one barrier per tile; two workgroups share a CU (d = 64, 128),
+//     so on each SIMD one wave's softmax can overlap the other's MFMA work.
 #include <type_traits>
 
 #include "internal.h"
@@ -46,10 +46,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-constexpr int kBM = 128;       // query rows per workgroup (4 waves x 32)
-constexpr int kBN = 64;        // keys per K/V tile
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
+constexpr int kBN = 64;                        // keys per K/V tile
 constexpr int32_t kRsrcWord3 = 0x00020000;     // raw buffer, 32-bit data format (gfx9 family)
 constexpr uint32_t kOutOfRange = 0x7ffffff0u;  // a buffer offset past every num_records: the load returns 0
 constexpr float kRescaleSlack = 8.0f;          // log2 units the running maximum may exceed the reference by
@@ -65,14 +62,16 @@ struct Geom {
   static constexpr int TILE_BYTES = kBN * ROW_BYTES;
   static constexpr int INSTR = TILE_BYTES / 1024; // wave-wide 16-byte-per-lane copies per tile
   static constexpr int ROWS_PER_INSTR = 1024 / ROW_BYTES;
-  static_assert(INSTR % kWaves == 0, "tile copy must split evenly over the waves");
 };
 
-// Chunk swizzles (see the header comment). K: row p of the tile; V: row j of the tile.
+// Chunk swizzles (XOR on the 16-byte chunk index within a row), chosen for 64 four-byte LDS banks (256 bytes
+// per clock). K: row p of the tile, read 16 bytes per lane by 16 consecutive rows at one chunk index -> the 16
+// rows must land on 16 different bank groups. V: row j of the tile, read 8 bytes per lane by the transpose
+// reads, 32 lanes covering 4 consecutive rows x 64 bytes -> the 4 rows' 64-byte column groups must not overlap.
 template <int D>
-__device__ __forceinline__ int k_swz(int p) { return D == 24 ? (p >> 1) & 3 : p & 7; }
+__device__ __forceinline__ int k_swz(int p) { return D == 128 ? p & 15 : D == 64 ? (p >> 1) & 7 : (p >> 2) & 3; }
 template <int D>
-__device__ __forceinline__ int v_swz(int j) { return D == 24 ? 2 * ((j >> 1) & 1) : 2 * (j & 3); }
+__device__ __forceinline__ int v_swz(int j) { return D == 128 ? 4 * (j & 3) : D == 64 ? 4 * ((j >> 1) & 1) : 0; }
 // key held by LDS row p of a tile: bits 2 and 3 swapped inside each 32-key chunk (an involution)
 __device__ __forceinline__ int key_of_row(int p) { return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1); }
 
@@ -92,49 +91,78 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Issue this wave's share of the HBM -> LDS copy of K and V tile rows [j0, j0 + kBN).
-template <int D>
-__device__ __forceinline__ void issue_tile_copy(const __bf16* K, const __bf16* V, int j0, int Nk, char* ks, char* vs,
-                                                int wave, int lane) {
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+// This wave's share (of NW waves) of the HBM -> LDS copy of tile rows [j0, j0 + kBN) of K (IS_K: rows permuted,
+// chunks K-swizzled) or of V (chunks V-swizzled). Rows past Nk read as zero.
+template <int D, bool IS_K, int NW>
+__device__ __forceinline__ void issue_copy(const __bf16* X, int j0, int Nk, char* dst, int wave, int lane) {
   using G = Geom<D>;
+  static_assert(G::INSTR % NW == 0, "tile copy must split evenly over the waves");
   const int rows_valid = min(kBN, Nk - j0);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + (int64_t)j0 * D, (int64_t)rows_valid * D * 2);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + (int64_t)j0 * D, (int64_t)rows_valid * D * 2);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(X + (int64_t)j0 * D, (int64_t)rows_valid * D * 2);
   const int sub = lane / G::CPR, pos = lane % G::CPR;
 #pragma unroll
-  for (int i = 0; i < G::INSTR / kWaves; ++i) {
-    const int instr = wave * (G::INSTR / kWaves) + i;
+  for (int i = 0; i < G::INSTR / NW; ++i) {
+    const int instr = wave * (G::INSTR / NW) + i;
     const int row = instr * G::ROWS_PER_INSTR + sub;
-    const int mk = pos ^ k_swz<D>(row);
-    const int mv = pos ^ v_swz<D>(row);
-    const uint32_t ok = mk < G::CPG ? (uint32_t)((key_of_row(row) * D + mk * 8) * 2) : kOutOfRange;
-    const uint32_t ov = mv < G::CPG ? (uint32_t)((row * D + mv * 8) * 2) : kOutOfRange;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(ks + instr * 1024), 16, ok, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vs + instr * 1024), 16, ov, 0, 0, 0);
+    const int m = pos ^ (IS_K ? k_swz<D>(row) : v_swz<D>(row));
+    const int src_row = IS_K ? key_of_row(row) : row;
+    const uint32_t off = m < G::CPG ? (uint32_t)((src_row * D + m * 8) * 2) : kOutOfRange;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(dst + instr * 1024), 16, off, 0, 0, 0);
   }
 }
 
-__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+// Per-lane pieces of the LDS addressing, fixed for the whole key loop.
+template <int D>
+struct LaneAddr {
+  int k_row;                 // byte offset of this lane's K row (row l%32 of the first 32-key chunk)
+  int k_xor;                 // its chunk swizzle
+  int hi;                    // lane / 32: which 8-column half of each 16-wide k-step this lane supplies
+  int v[Geom<D>::CT];        // byte offset of this lane's first transpose read, per 32-column tile of O^T
+  __device__ LaneAddr(int lane) {
+    using G = Geom<D>;
+    const int l32 = lane & 31;
+    hi = lane >> 5;
+    k_row = l32 * G::ROW_BYTES;
+    k_xor = k_swz<D>(l32);
+    const int g2 = (lane >> 4) & 1, a4 = (lane & 15) >> 2, b4 = lane & 3;
+    const int row = 8 * hi + a4;                      // key row of the first transpose read
+#pragma unroll
+    for (int ct = 0; ct < G::CT; ++ct) {
+      const int m = 4 * ct + 2 * g2 + (b4 >> 1);     // 16-byte chunk of columns 32*ct + 16*g2 + 4*b4 .. +3
+      v[ct] = row * G::ROW_BYTES + 16 * (m ^ v_swz<D>(row)) + 8 * (b4 & 1);
+    }
+  }
+};
 
-// One 64-key tile for this wave's 32 query rows. KB / VB: byte offsets of the tile's K and V buffers in LDS
-// (compile-time, so they fold into the instructions' offset fields). `partial` tiles apply the mask.
-template <int D, int KB, int VB>
-__device__ __forceinline__ void compute_tile(const char* smem, const bf16x8 (&qf)[Geom<D>::KSTEPS],
-                                             f32x16 (&acc)[Geom<D>::CT], float& m_ref, float& l_run, float& lq_run, bool partial,
-                                             int lim, float scale_log2, int k_row, int k_xor, int hi,
-                                             const int (&v_addr)[Geom<D>::CT]) {
+// S^T = K . Q^T for one 64-key tile (K tile at `kt` in LDS) and this wave's 32 query rows: keys 0..31 into s0,
+// keys 32..63 into s1.
+template <int D>
+__device__ __forceinline__ void qk_tile(const char* kt, const bf16x8 (&qf)[Geom<D>::KSTEPS], f32x16& s0, f32x16& s1,
+                                        const LaneAddr<D>& la) {
   using G = Geom<D>;
-  // S^T chunks: keys 0..31 (s0) and 32..63 (s1) of the tile against this wave's 32 query rows.
-  f32x16 s0 = {}, s1 = {};
+  s0 = f32x16{};
+  s1 = f32x16{};
 #pragma unroll
   for (int kc = 0; kc < G::KSTEPS; ++kc) {
-    const char* p = smem + KB + k_row + 16 * ((2 * kc + hi) ^ k_xor);
+    const char* p = kt + la.k_row + 16 * ((2 * kc + la.hi) ^ la.k_xor);
     const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(p);
     const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(p + 32 * G::ROW_BYTES);
     s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[kc], s0, 0, 0, 0);
     s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[kc], s1, 0, 0, 0);
   }
-  // Register r of lane l holds key 16*(r/8) + 8*(l/32) + r%8 of its 32-key chunk, for query row l%32.
+}
+
+// Online softmax of one tile's scores. `partial` tiles apply the mask: register r of lane l holds key
+// 16*(r/8) + 8*(l/32) + r%8 of its 32-key chunk, for query row l%32; keys past `lim` (relative to this lane's
+// first key of the tile) are hidden. Writes the bf16 weights pb (B operands of P.V, 16 keys each), rescales
+// acc when the reference maximum moves, and updates both row sums.
+template <int D>
+__device__ __forceinline__ void softmax_tile(f32x16 s0, f32x16 s1, bf16x8 (&pb)[4], f32x16 (&acc)[Geom<D>::CT],
+                                             float& m_ref, float& l_run, float& lq_run, bool partial, int lim,
+                                             float scale_log2) {
+  using G = Geom<D>;
   if (partial) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -165,31 +193,34 @@ __device__ __forceinline__ void compute_tile(const char* smem, const bf16x8 (&qf
 #pragma unroll
     for (int ct = 0; ct < G::CT; ++ct) acc[ct] *= alpha;
   }
-
-  bf16x8 pb[4];
   pb[0] = __builtin_convertvector(__builtin_shufflevector(s0, s0, 0, 1, 2, 3, 4, 5, 6, 7), bf16x8);
   pb[1] = __builtin_convertvector(__builtin_shufflevector(s0, s0, 8, 9, 10, 11, 12, 13, 14, 15), bf16x8);
   pb[2] = __builtin_convertvector(__builtin_shufflevector(s1, s1, 0, 1, 2, 3, 4, 5, 6, 7), bf16x8);
   pb[3] = __builtin_convertvector(__builtin_shufflevector(s1, s1, 8, 9, 10, 11, 12, 13, 14, 15), bf16x8);
-  // Two row sums: l_run over the fp32 weights gives the log-sum-exp; lq_run over the bf16-rounded weights that
-  // enter P.V (one packed dot with (1, 1) per pair) normalises O, so numerator and denominator use the same
-  // weights and a constant V comes back exactly.
+  // Row sum of the bf16-rounded weights (one packed dot with (1, 1) per pair): normalises O.
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  float psum0 = 0.0f, psum1 = 0.0f;
+  float q0 = 0.0f, q1 = 0.0f;
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    psum0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[kk], pb[kk], 0, 1), ones, psum0, false);
-    psum1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[kk], pb[kk], 2, 3), ones, psum1, false);
-    psum0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[kk], pb[kk], 4, 5), ones, psum0, false);
-    psum1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[kk], pb[kk], 6, 7), ones, psum1, false);
+    q0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[kk], pb[kk], 0, 1), ones, q0, false);
+    q1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[kk], pb[kk], 2, 3), ones, q1, false);
+    q0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[kk], pb[kk], 4, 5), ones, q0, false);
+    q1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[kk], pb[kk], 6, 7), ones, q1, false);
   }
-  lq_run = __builtin_fmaf(alpha, lq_run, psum0 + psum1);
-  // V^T operand via two transpose reads: slots 0-3 from key rows +0..3, slots 4-7 from +4..7 of the 8-key group.
+  lq_run = __builtin_fmaf(alpha, lq_run, q0 + q1);
+}
+
+// acc += P . V for one tile (V tile at `vt` in LDS): V^T operand via two transpose reads, slots 0-3 from key
+// rows +0..3 and slots 4-7 from rows +4..7 of each 8-key group.
+template <int D>
+__device__ __forceinline__ void pv_tile(const char* vt, const bf16x8 (&pb)[4], f32x16 (&acc)[Geom<D>::CT],
+                                        const LaneAddr<D>& la) {
+  using G = Geom<D>;
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
     for (int ct = 0; ct < G::CT; ++ct) {
-      const char* p = smem + VB + v_addr[ct] + kk * 16 * G::ROW_BYTES;
+      const char* p = vt + la.v[ct] + kk * 16 * G::ROW_BYTES;
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
       const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * G::ROW_BYTES));
       const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -198,138 +229,152 @@ __device__ __forceinline__ void compute_tile(const char* smem, const bf16x8 (&qf
   }
 }
 
-template <int D, bool OF32>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
+// Q^T fragment (B operand) of this wave's 32 rows starting at `row0` of the workgroup's block: lane holds row
+// row0 + l%32, head-dim columns 16*kc + 8*(l/32) .. +7; rows past the block read as zero.
+template <int D>
+__device__ __forceinline__ void load_q(const __bf16* Qblk, int rows_valid, int row0, int lane,
+                                       bf16x8 (&qf)[Geom<D>::KSTEPS]) {
   using G = Geom<D>;
-  __shared__ __attribute__((aligned(1024))) char smem[4 * G::TILE_BYTES];   // K0 V0 K1 V1
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qblk, (int64_t)rows_valid * D * 2);
   const int l32 = lane & 31, hi = lane >> 5;
-
-  // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a contiguous range of (batch, head)
-  // slices so that a slice's K/V tiles are re-read from one L2. Within a slice the heaviest causal tile (the
-  // last query rows) goes first.
-  int64_t w = blockIdx.x;
-  if (xcd_remap) w = (w & 7) * ((int64_t)gridDim.x >> 3) + (w >> 3);
-  const int64_t bh = w / n_qtiles;
-  const int qt = n_qtiles - 1 - (int)(w % n_qtiles);
-  const int q0 = qt * kBM;
-
-  const __bf16* Q = reinterpret_cast<const __bf16*>(a.q) + (bh * (int64_t)a.Nq + q0) * D;
-  const __bf16* K = reinterpret_cast<const __bf16*>(a.k) + bh * (int64_t)a.Nk * D;
-  const __bf16* V = reinterpret_cast<const __bf16*>(a.v) + bh * (int64_t)a.Nk * D;
-
-  const int qlast = min(q0 + kBM, a.Nq) - 1;
-  const int kend = a.causal ? min(a.Nk, qlast + a.diag + 1) : a.Nk;
-  const int ntiles = kend > 0 ? (kend + kBN - 1) / kBN : 0;
-  const int kfull = a.causal ? min(a.Nk, q0 + a.diag + 1) : a.Nk;   // keys visible to every row of the tile
-  const int nfull = kfull > 0 ? kfull / kBN : 0;
-  // keys any row of this wave can see end here: this wave skips the compute of later tiles (it still copies)
-  const int wave_kend = a.causal ? min(a.Nk, q0 + wave * 32 + 31 + a.diag + 1) : a.Nk;
-
-  if (ntiles > 0) issue_tile_copy<D>(K, V, 0, a.Nk, smem, smem + G::TILE_BYTES, wave, lane);
-
-  // Q^T fragment (B operand): lane holds query row 32*wave + l32, head-dim columns 16*kc + 8*hi .. +7.
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q, (int64_t)min(kBM, a.Nq - q0) * D * 2);
-  bf16x8 qf[G::KSTEPS];
 #pragma unroll
   for (int kc = 0; kc < G::KSTEPS; ++kc) {
     const int c = kc * 16 + 8 * hi;
-    const uint32_t off = c < D ? (uint32_t)(((wave * 32 + l32) * D + c) * 2) : kOutOfRange;
+    const uint32_t off = c < D ? (uint32_t)(((row0 + l32) * D + c) * 2) : kOutOfRange;
     qf[kc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
   }
+}
 
-  // Per-lane LDS addressing, fixed for the whole loop.
-  const int k_row = l32 * G::ROW_BYTES;
-  const int k_xor = k_swz<D>(l32);
-  int v_addr[G::CT];
-  {
-    const int g2 = (lane >> 4) & 1, a4 = (lane & 15) >> 2, b4 = lane & 3;
-    const int row = 8 * hi + a4;                      // key row of the first transpose read (kk = 0)
+// Epilogue: O = acc / lq, lse = ln2 * (m + log2 l); a row with no visible key gives (0, -inf). Register r of O^T
+// tile ct holds head-dim column 32*ct + 8*(r/4) + 4*hi + r%4 of this lane's row; the buffer range of the
+// workgroup's block drops the stores of rows past Nq.
+template <int D, bool OF32>
+__device__ __forceinline__ void store_out(const FwdArgs& a, int64_t bh, int q0, int block_rows, int local_row, int lane,
+                                          const f32x16 (&acc)[Geom<D>::CT], float m_ref, float l_run, float lq_run) {
+  using G = Geom<D>;
+  const int hi = lane >> 5;
+  const float l_tot = pair_sum(l_run);
+  const float lq_tot = pair_sum(lq_run);
+  const float inv = lq_tot > 0.0f ? 1.0f / lq_tot : 0.0f;
+  const int qi = q0 + local_row;
+  if (hi == 0 && qi < a.Nq)
+    a.lse[bh * (int64_t)a.Nq + qi] =
+        l_tot > 0.0f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f : -INFINITY;
+  const int64_t o_rows = min(block_rows, a.Nq - q0);
+  const int64_t base = (bh * (int64_t)a.Nq + q0) * D;
+  const __amdgpu_buffer_rsrc_t ro = OF32 ? make_rsrc(reinterpret_cast<float*>(a.o) + base, o_rows * D * 4)
+                                         : make_rsrc(reinterpret_cast<__bf16*>(a.o) + base, o_rows * D * 2);
 #pragma unroll
-    for (int ct = 0; ct < G::CT; ++ct) {
-      const int m = 4 * ct + 2 * g2 + (b4 >> 1);     // 16-byte chunk of columns 32*ct + 16*g2 + 4*b4 .. +3
-      v_addr[ct] = row * G::ROW_BYTES + 16 * (m ^ v_swz<D>(row)) + 8 * (b4 & 1);
+  for (int ct = 0; ct < G::CT; ++ct)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int c = ct * 32 + 8 * g + 4 * hi;
+      if (c >= D) continue;
+      const f32x4 y = {acc[ct][4 * g] * inv, acc[ct][4 * g + 1] * inv, acc[ct][4 * g + 2] * inv,
+                       acc[ct][4 * g + 3] * inv};
+      if (OF32)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, y), ro, (uint32_t)((local_row * D + c) * 4), 0, 0);
+      else
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, __builtin_convertvector(y, bf16x4)), ro,
+                                              (uint32_t)((local_row * D + c) * 2), 0, 0);
     }
+}
+
+// Workgroup -> (batch*head slice, query block). Workgroups are dispatched round-robin over the 8 XCDs; each XCD
+// gets a contiguous range of slices so that a slice's K/V tiles are re-read from one L2. Within a slice the
+// heaviest causal block (the last query rows) goes first.
+__device__ __forceinline__ void decode_block(int n_qtiles, int xcd_remap, int64_t& bh, int& qt) {
+  int64_t w = blockIdx.x;
+  if (xcd_remap) w = (w & 7) * ((int64_t)gridDim.x >> 3) + (w >> 3);
+  bh = w / n_qtiles;
+  qt = n_qtiles - 1 - (int)(w % n_qtiles);
+}
+
+// ------------------------------------------------------------------------------------------------------------
+// The kernel: 4 waves, 128 query rows, one barrier per tile; the copy of tile t+1 is issued right after the
+// barrier of tile t into the slots tile t-1 left.
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRows = 32 * kWaves;
+
+// Waves per SIMD the register budget allows (512 VGPRs per SIMD lane): d = 128 needs ~210 registers (two waves,
+// two workgroups of 64 KB LDS per CU), d = 64 ~135 (three), d = 24 ~90 (four).
+template <int D>
+constexpr int waves_per_simd() { return D >= 128 ? 2 : D >= 64 ? 3 : 4; }
+
+template <int D, bool OF32>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(waves_per_simd<D>(), waves_per_simd<D>())))
+void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
+  using G = Geom<D>;
+  constexpr int T = G::TILE_BYTES;
+  // Four separate LDS arrays (K slots 0/1, V slots 0/1), always named at compile time: the compiler can then
+  // tell that a tile copy in flight into one slot does not alias operand reads from another, and does not stall
+  // those reads on the copy; the explicit vmcnt wait before each barrier orders the copies.
+  __shared__ __attribute__((aligned(1024))) char k0[T];
+  __shared__ __attribute__((aligned(1024))) char k1[T];
+  __shared__ __attribute__((aligned(1024))) char v0[T];
+  __shared__ __attribute__((aligned(1024))) char v1[T];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int64_t bh;
+  int qt;
+  decode_block(n_qtiles, xcd_remap, bh, qt);
+  const int q0 = qt * kRows;
+  const __bf16* K = reinterpret_cast<const __bf16*>(a.k) + bh * (int64_t)a.Nk * D;
+  const __bf16* V = reinterpret_cast<const __bf16*>(a.v) + bh * (int64_t)a.Nk * D;
+
+  const int qlast = min(q0 + kRows, a.Nq) - 1;
+  const int kend = a.causal ? min(a.Nk, qlast + a.diag + 1) : a.Nk;
+  const int ntiles = kend > 0 ? (kend + kBN - 1) / kBN : 0;
+  const int wrow0 = q0 + wave * 32;
+  const int wkfull = a.causal ? min(a.Nk, wrow0 + a.diag + 1) : a.Nk;
+  const int nfull = wkfull > 0 ? wkfull / kBN : 0;
+  const int wkend = a.causal ? min(a.Nk, wrow0 + 31 + a.diag + 1) : a.Nk;
+
+  if (ntiles > 0) {
+    issue_copy<D, true, kWaves>(K, 0, a.Nk, k0, wave, lane);
+    issue_copy<D, false, kWaves>(V, 0, a.Nk, v0, wave, lane);
   }
+  bf16x8 qf[G::KSTEPS];
+  load_q<D>(reinterpret_cast<const __bf16*>(a.q) + (bh * (int64_t)a.Nq + q0) * D, min(kRows, a.Nq - q0),
+            wave * 32, lane, qf);
+  const LaneAddr<D> la(lane);
+  const int row_lim = (a.causal ? min(wrow0 + (lane & 31) + a.diag, a.Nk - 1) : a.Nk - 1) - 8 * la.hi;
 
   f32x16 acc[G::CT];
 #pragma unroll
   for (int ct = 0; ct < G::CT; ++ct) acc[ct] = f32x16{};
   float m_ref = -INFINITY, l_run = 0.0f, lq_run = 0.0f;
-  const int qi = q0 + wave * 32 + l32;     // this lane's query row
-  const int row_lim = (a.causal ? min(qi + a.diag, a.Nk - 1) : a.Nk - 1) - 8 * hi;
-
-  // Tile t lives in buffer t & 1. Before tile t is read: this wave's copies have landed (vmcnt), then the
-  // barrier guarantees every wave's copies have landed and every wave has finished tile t-1, whose buffer the
-  // copy of tile t+1 then overwrites.
-  auto step = [&](auto buf_tag, int t) {
-    constexpr int B = decltype(buf_tag)::value;
-    constexpr int KB = B ? 2 * G::TILE_BYTES : 0, VB = KB + G::TILE_BYTES;
-    constexpr int KN = B ? 0 : 2 * G::TILE_BYTES, VN = KN + G::TILE_BYTES;
-    wait_vmem_all();
-    __syncthreads();
-    if (t + 1 < ntiles) issue_tile_copy<D>(K, V, (t + 1) * kBN, a.Nk, smem + KN, smem + VN, wave, lane);
-    if (t * kBN < wave_kend)
-      compute_tile<D, KB, VB>(smem, qf, acc, m_ref, l_run, lq_run, t >= nfull, row_lim - t * kBN, a.scale_log2, k_row,
-                              k_xor, hi, v_addr);
+  auto step = [&](int t, const char* kc, const char* vc, char* kn, char* vn) {
+    wait_vmem_all();      // this wave's copies of tile t have landed
+    __syncthreads();      // every wave's copies have landed; every wave is done with tile t-1
+    if (t + 1 < ntiles) {
+      issue_copy<D, true, kWaves>(K, (t + 1) * kBN, a.Nk, kn, wave, lane);
+      issue_copy<D, false, kWaves>(V, (t + 1) * kBN, a.Nk, vn, wave, lane);
+    }
+    if (t * kBN >= wkend) return;
+    f32x16 s0, s1;
+    bf16x8 pb[4];
+    qk_tile<D>(kc, qf, s0, s1, la);
+    softmax_tile<D>(s0, s1, pb, acc, m_ref, l_run, lq_run, t >= nfull, row_lim - t * kBN, a.scale_log2);
+    pv_tile<D>(vc, pb, acc, la);
   };
   for (int t = 0; t < ntiles; t += 2) {
-    step(std::integral_constant<int, 0>{}, t);
-    if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, t + 1);
+    step(t, k0, v0, k1, v1);
+    if (t + 1 < ntiles) step(t + 1, k1, v1, k0, v0);
   }
-
-  // Epilogue: O = acc / l, lse = ln2 * (m + log2 l); a row with no visible key gives (0, -inf).
-  const float l_tot = pair_sum(l_run);
-  const float lq_tot = pair_sum(lq_run);
-  const float inv = lq_tot > 0.0f ? 1.0f / lq_tot : 0.0f;
-  if (hi == 0 && qi < a.Nq)
-    a.lse[bh * (int64_t)a.Nq + qi] =
-        l_tot > 0.0f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f : -INFINITY;
-  const int64_t o_rows = min(kBM, a.Nq - q0);
-  const int local_row = wave * 32 + l32;
-  // Register r of O^T tile ct holds head-dim column 32*ct + 8*(r/4) + 4*hi + r%4 of this lane's row; the
-  // buffer range drops the stores of rows past Nq.
-  if (OF32) {
-    const __amdgpu_buffer_rsrc_t ro =
-        make_rsrc(reinterpret_cast<float*>(a.o) + (bh * (int64_t)a.Nq + q0) * D, o_rows * D * 4);
-#pragma unroll
-    for (int ct = 0; ct < G::CT; ++ct)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int c = ct * 32 + 8 * g + 4 * hi;
-        if (c >= D) continue;
-        const f32x4 y = {acc[ct][4 * g] * inv, acc[ct][4 * g + 1] * inv, acc[ct][4 * g + 2] * inv,
-                         acc[ct][4 * g + 3] * inv};
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, y), ro, (uint32_t)((local_row * D + c) * 4), 0, 0);
-      }
-  } else {
-    const __amdgpu_buffer_rsrc_t ro =
-        make_rsrc(reinterpret_cast<__bf16*>(a.o) + (bh * (int64_t)a.Nq + q0) * D, o_rows * D * 2);
-#pragma unroll
-    for (int ct = 0; ct < G::CT; ++ct)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int c = ct * 32 + 8 * g + 4 * hi;
-        if (c >= D) continue;
-        const f32x4 y = {acc[ct][4 * g] * inv, acc[ct][4 * g + 1] * inv, acc[ct][4 * g + 2] * inv,
-                         acc[ct][4 * g + 3] * inv};
-        const bf16x4 b = __builtin_convertvector(y, bf16x4);
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, b), ro, (uint32_t)((local_row * D + c) * 2), 0, 0);
-      }
-  }
+  store_out<D, OF32>(a, bh, q0, kRows, wave * 32 + (lane & 31), lane, acc, m_ref, l_run, lq_run);
 }
 
 template <int D, bool OF32>
 hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
-  const int n_qtiles = (a.Nq + kBM - 1) / kBM;
+  const int n_qtiles = (a.Nq + kRows - 1) / kRows;
   const int64_t total = (int64_t)n_qtiles * a.BH;
   if (total > 0x7fffffff) return hipErrorInvalidConfiguration;
   const int remap = (total % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, OF32>), dim3((unsigned)total), dim3(kThreads), 0, stream, a, n_qtiles,
-                     remap);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, OF32>), dim3((unsigned)total), dim3(kThreads), 0, stream, a,
+                     n_qtiles, remap);
   return hipGetLastError();
 }
 
