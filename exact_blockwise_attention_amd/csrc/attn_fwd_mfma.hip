@@ -40,6 +40,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -136,97 +137,276 @@ struct LaneAddr {
   }
 };
 
-// S^T = K . Q^T for one 64-key tile (K tile at `kt` in LDS) and this wave's 32 query rows: keys 0..31 into s0,
-// keys 32..63 into s1.
+// K operand of MFMA i of S^T = K . Q^T over one 64-key tile (K tile at `kt` in LDS): k-step i/2, keys
+// 32*(i%2) .. +31 (lane: key row l%32, head-dim columns 16*(i/2) + 8*(l/32) .. +7).
 template <int D>
+__device__ __forceinline__ bf16x8 k_frag(const char* kt, const LaneAddr<D>& la, int i) {
+  const char* p = kt + la.k_row + 16 * ((2 * (i >> 1) + la.hi) ^ la.k_xor) + (i & 1) * 32 * Geom<D>::ROW_BYTES;
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// V^T operand of MFMA j of O^T += V^T . P^T (V tile at `vt` in LDS): keys 16*(j/CT) .. +15, head-dim columns
+// 32*(j%CT) .. +31, gathered by two transpose reads (slots 0-3 from key rows +0..3 and slots 4-7 from rows
+// +4..7 of each 8-key group).
+template <int D>
+__device__ __forceinline__ bf16x8 v_frag(const char* vt, const LaneAddr<D>& la, int j) {
+  using G = Geom<D>;
+  const char* p = vt + la.v[j % G::CT] + (j / G::CT) * 16 * G::ROW_BYTES;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * G::ROW_BYTES));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Marks a value as produced here: an empty asm statement that takes it in and out of registers, so that the
+// optimiser cannot sink its computation into a later block (it emits no instruction).
+__device__ __forceinline__ void pin(bf16x8& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// S^T = K . Q^T for one 64-key tile and this wave's 32 query rows: keys 0..31 into s0, keys 32..63 into s1. With
+// FENCED, the LDS reads run two MFMAs ahead in a ring of three registers and the order is fixed slot by slot
+// (the pipelined kernel keeps two score tiles live and cannot afford the reads hoisted further).
+template <int D, bool FENCED = false>
 __device__ __forceinline__ void qk_tile(const char* kt, const bf16x8 (&qf)[Geom<D>::KSTEPS], f32x16& s0, f32x16& s1,
                                         const LaneAddr<D>& la) {
   using G = Geom<D>;
-  s0 = f32x16{};
-  s1 = f32x16{};
+  if constexpr (FENCED) {
+    constexpr int NM = 2 * G::KSTEPS;
+    bf16x8 kf[3];
+    kf[0] = k_frag<D>(kt, la, 0);
+    kf[1] = k_frag<D>(kt, la, 1);
 #pragma unroll
-  for (int kc = 0; kc < G::KSTEPS; ++kc) {
-    const char* p = kt + la.k_row + 16 * ((2 * kc + la.hi) ^ la.k_xor);
-    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(p);
-    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(p + 32 * G::ROW_BYTES);
-    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[kc], s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[kc], s1, 0, 0, 0);
-  }
-}
-
-// Online softmax of one tile's scores. `partial` tiles apply the mask: register r of lane l holds key
-// 16*(r/8) + 8*(l/32) + r%8 of its 32-key chunk, for query row l%32; keys past `lim` (relative to this lane's
-// first key of the tile) are hidden. Writes the bf16 weights pb (B operands of P.V, 16 keys each), rescales
-// acc when the reference maximum moves, and updates both row sums.
-template <int D>
-__device__ __forceinline__ void softmax_tile(f32x16 s0, f32x16 s1, bf16x8 (&pb)[4], f32x16 (&acc)[Geom<D>::CT],
-                                             float& m_ref, float& l_run, float& lq_run, bool partial, int lim,
-                                             float scale_log2) {
-  using G = Geom<D>;
-  if (partial) {
+    for (int i = 0; i < NM; ++i) {
+      if (i + 2 < NM) kf[(i + 2) % 3] = k_frag<D>(kt, la, i + 2);
+      if (i & 1)
+        s1 = mfma(kf[i % 3], qf[i >> 1], i < 2 ? f32x16{} : s1);
+      else
+        s0 = mfma(kf[i % 3], qf[i >> 1], i < 2 ? f32x16{} : s0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    s0 = f32x16{};
+    s1 = f32x16{};
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int kr = 16 * (r >> 3) + (r & 7);
-      if (kr > lim) s0[r] = -INFINITY;
-      if (kr + 32 > lim) s1[r] = -INFINITY;
+    for (int kc = 0; kc < G::KSTEPS; ++kc) {
+      s0 = mfma(k_frag<D>(kt, la, 2 * kc), qf[kc], s0);
+      s1 = mfma(k_frag<D>(kt, la, 2 * kc + 1), qf[kc], s1);
     }
   }
-  // IEEE maximum (v_maximum3_f32): no NaN quieting of the MFMA results is needed before it.
-  float mx = __builtin_elementwise_maximum(s0[0], s1[0]);
-#pragma unroll
-  for (int r = 1; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s0[r], s1[r]));
-  const float mt = pair_max(mx) * scale_log2;
-  const bool need = mt > m_ref + kRescaleSlack;
-  const float m_new = need ? mt : m_ref;
-  const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
-  m_ref = m_new;
-  const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-  float psum = 0.0f;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    s0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], scale_log2, -m_use));
-    s1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], scale_log2, -m_use));
-    psum += s0[r] + s1[r];
-  }
-  l_run = __builtin_fmaf(alpha, l_run, psum);
-  if (__builtin_amdgcn_ballot_w64(need)) {
-#pragma unroll
-    for (int ct = 0; ct < G::CT; ++ct) acc[ct] *= alpha;
-  }
-  pb[0] = __builtin_convertvector(__builtin_shufflevector(s0, s0, 0, 1, 2, 3, 4, 5, 6, 7), bf16x8);
-  pb[1] = __builtin_convertvector(__builtin_shufflevector(s0, s0, 8, 9, 10, 11, 12, 13, 14, 15), bf16x8);
-  pb[2] = __builtin_convertvector(__builtin_shufflevector(s1, s1, 0, 1, 2, 3, 4, 5, 6, 7), bf16x8);
-  pb[3] = __builtin_convertvector(__builtin_shufflevector(s1, s1, 8, 9, 10, 11, 12, 13, 14, 15), bf16x8);
-  // Row sum of the bf16-rounded weights (one packed dot with (1, 1) per pair): normalises O.
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  float q0 = 0.0f, q1 = 0.0f;
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    q0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[kk], pb[kk], 0, 1), ones, q0, false);
-    q1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[kk], pb[kk], 2, 3), ones, q1, false);
-    q0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[kk], pb[kk], 4, 5), ones, q0, false);
-    q1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[kk], pb[kk], 6, 7), ones, q1, false);
-  }
-  lq_run = __builtin_fmaf(alpha, lq_run, q0 + q1);
 }
 
-// acc += P . V for one tile (V tile at `vt` in LDS): V^T operand via two transpose reads, slots 0-3 from key
-// rows +0..3 and slots 4-7 from rows +4..7 of each 8-key group.
+// The softmax works on one tile's 32 scores per lane as scalars, w[16*h + r] = register r of score accumulator h
+// (h = 0: keys 0..31 of the tile, h = 1: keys 32..63): lane l holds key 32*h + 16*(r/8) + 8*(l/32) + r%8, for
+// query row l%32. Scalars rather than in-place vector updates keep the register allocator from copying whole
+// 16-register accumulators.
+__device__ __forceinline__ void unpack_scores(const f32x16& s0, const f32x16& s1, float (&w)[32]) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    w[r] = s0[r];
+    w[16 + r] = s1[r];
+  }
+}
+
+// bf16 B operand of P.V for keys 16*kk .. +15 of the tile, from weights w[8*kk .. 8*kk + 7].
+__device__ __forceinline__ bf16x8 pack_weights(const float (&w)[32], int kk) {
+  const f32x8 v = {w[8 * kk], w[8 * kk + 1], w[8 * kk + 2], w[8 * kk + 3],
+                   w[8 * kk + 4], w[8 * kk + 5], w[8 * kk + 6], w[8 * kk + 7]};
+  return __builtin_convertvector(v, bf16x8);
+}
+
+// Hides the keys of a tile that straddles the causal diagonal: keys past `lim` (relative to this lane's first
+// key of the tile) are hidden.
+__device__ __forceinline__ void mask_tile(float (&w)[32], int lim) {
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    const int r = e & 15;
+    if (32 * (e >> 4) + 16 * (r >> 3) + (r & 7) > lim) w[e] = -INFINITY;
+  }
+}
+
+// Online softmax, first half (also the reference update of the pipelined stage): the tile's row maximum moves
+// the reference maximum when it exceeds it by more than the slack; `alpha` is the factor that rescales everything
+// accumulated so far (1 when the reference did not move); m_use is the reference the weights are taken against.
+__device__ __forceinline__ void update_reference(float mx, float& m_ref, float& alpha, bool& need, float& m_use,
+                                                 float scale_log2) {
+  const float mt = pair_max(mx) * scale_log2;
+  need = mt > m_ref + kRescaleSlack;
+  const float m_new = need ? mt : m_ref;
+  alpha = need ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
+  m_ref = m_new;
+  m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+}
+
+__device__ __forceinline__ float weight(float s, float scale_log2, float m_use) {
+  return __builtin_amdgcn_exp2f(__builtin_fmaf(s, scale_log2, -m_use));
+}
+
+// The scores become exp2 weights relative to the reference, in place (fp32, kept for the row sum) and rounded to
+// bf16 in pb (the B operands of P.V, 16 keys each).
+__device__ __forceinline__ void weights_tile(float (&w)[32], bf16x8 (&pb)[4], float& m_ref, float& alpha, bool& need,
+                                             float scale_log2) {
+  // IEEE maximum (v_maximum3_f32): no NaN quieting of the MFMA results is needed before it.
+  float mx = __builtin_elementwise_maximum(w[0], w[1]);
+#pragma unroll
+  for (int e = 2; e < 32; e += 2) mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(w[e], w[e + 1]));
+  float m_use;
+  update_reference(mx, m_ref, alpha, need, m_use, scale_log2);
+#pragma unroll
+  for (int e = 0; e < 32; ++e) w[e] = weight(w[e], scale_log2, m_use);
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) pb[kk] = pack_weights(w, kk);
+}
+
+// Online softmax, second half: both running row sums. l_run sums the fp32 weights (it gives the log-sum-exp);
+// lq_run sums the bf16-rounded weights that enter P.V (one packed dot with (1, 1) per pair; it normalises O).
+// (The pair is picked with constant shuffles: reading it as element `pr` of the vector reinterpreted as four
+// 32-bit words gave element 0 for every `pr` with this compiler.)
+__device__ __forceinline__ float dot_pair(const bf16x8& v, int pr, float acc) {
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  bf16x2 x;
+  switch (pr) {
+    case 0: x = __builtin_shufflevector(v, v, 0, 1); break;
+    case 1: x = __builtin_shufflevector(v, v, 2, 3); break;
+    case 2: x = __builtin_shufflevector(v, v, 4, 5); break;
+    default: x = __builtin_shufflevector(v, v, 6, 7); break;
+  }
+  return __builtin_amdgcn_fdot2_f32_bf16(x, ones, acc, false);
+}
+__device__ __forceinline__ void sums_tile(const float (&w)[32], const bf16x8 (&pb)[4], float alpha, float& l_run,
+                                          float& lq_run) {
+  float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int e = 0; e < 32; ++e) p[e & 3] += w[e];
+  float q[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int j = 0; j < 16; ++j) q[j & 3] = dot_pair(pb[j >> 2], j & 3, q[j & 3]);
+  l_run = __builtin_fmaf(alpha, l_run, (p[0] + p[1]) + (p[2] + p[3]));
+  lq_run = __builtin_fmaf(alpha, lq_run, (q[0] + q[1]) + (q[2] + q[3]));
+}
+
+// Rescales the accumulator when any lane's reference maximum moved.
 template <int D>
+__device__ __forceinline__ void rescale_acc(f32x16 (&acc)[Geom<D>::CT], float alpha, bool need) {
+  if (__builtin_amdgcn_ballot_w64(need)) {
+#pragma unroll
+    for (int ct = 0; ct < Geom<D>::CT; ++ct) acc[ct] *= alpha;
+  }
+}
+
+// acc += P . V for one tile (V tile at `vt` in LDS); FENCED as for qk_tile.
+template <int D, bool FENCED = false>
 __device__ __forceinline__ void pv_tile(const char* vt, const bf16x8 (&pb)[4], f32x16 (&acc)[Geom<D>::CT],
                                         const LaneAddr<D>& la) {
   using G = Geom<D>;
+  constexpr int NM = 4 * G::CT;
+  if constexpr (FENCED) {
+    bf16x8 vf[3];
+    vf[0] = v_frag<D>(vt, la, 0);
+    vf[1] = v_frag<D>(vt, la, 1);
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-    for (int ct = 0; ct < G::CT; ++ct) {
-      const char* p = vt + la.v[ct] + kk * 16 * G::ROW_BYTES;
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
-      const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * G::ROW_BYTES));
-      const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-      acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kk], acc[ct], 0, 0, 0);
+    for (int j = 0; j < NM; ++j) {
+      if (j + 2 < NM) vf[(j + 2) % 3] = v_frag<D>(vt, la, j + 2);
+      acc[j % G::CT] = mfma(vf[j % 3], pb[j / G::CT], acc[j % G::CT]);
+      __builtin_amdgcn_sched_barrier(0);
     }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NM; ++j) acc[j % G::CT] = mfma(v_frag<D>(vt, la, j), pb[j / G::CT], acc[j % G::CT]);
   }
+}
+
+// ------------------------------------------------------------------------------------------------------------
+// Software-pipelined stage (d = 128). A wave issues in order, and an MFMA keeps the matrix unit busy for 32
+// cycles during which the same wave can issue vector-ALU work that does not depend on it. Each stage therefore
+// lists its instructions slot by slot -- one MFMA, the LDS reads two MFMAs ahead, and a slice of the softmax work
+// of the current tile -- with a scheduling fence after every slot so that the compiler keeps that order.
+//
+// Phase 1: the 16 MFMAs of the next tile's scores, beside the current tile's row maximum (slots 0-3), reference
+// update (slot 4), the weights of keys 0..31 (slots 5-12) and their bf16 rounding (slots 10, 14).
+template <int D>
+__device__ __forceinline__ void stage_phase1(const char* kn, const bf16x8 (&qf)[Geom<D>::KSTEPS], f32x16& n0,
+                                             f32x16& n1, const LaneAddr<D>& la, float (&w)[32], bf16x8 (&pb)[4],
+                                             float& m_ref, float& alpha, bool& need, float& m_use, float scale_log2) {
+  constexpr int NM = 2 * Geom<D>::KSTEPS;
+  static_assert(NM == 16, "the slot plan below is laid out for 16 MFMAs per phase");
+  bf16x8 kf[3];
+  kf[0] = k_frag<D>(kn, la, 0);
+  kf[1] = k_frag<D>(kn, la, 1);
+  float pm[4];
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    if (i + 2 < NM) kf[(i + 2) % 3] = k_frag<D>(kn, la, i + 2);
+    if (i & 1)
+      n1 = mfma(kf[i % 3], qf[i >> 1], i < 2 ? f32x16{} : n1);
+    else
+      n0 = mfma(kf[i % 3], qf[i >> 1], i < 2 ? f32x16{} : n0);
+    if (i < 4) {
+      // IEEE maximum (v_maximum3_f32): no NaN quieting of the MFMA results is needed before it.
+      float m = __builtin_elementwise_maximum(w[8 * i], w[8 * i + 1]);
+#pragma unroll
+      for (int e = 2; e < 8; e += 2)
+        m = __builtin_elementwise_maximum(m, __builtin_elementwise_maximum(w[8 * i + e], w[8 * i + e + 1]));
+      pm[i] = m;
+    } else if (i == 4) {
+      const float mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(pm[0], pm[1]),
+                                                     __builtin_elementwise_maximum(pm[2], pm[3]));
+      update_reference(mx, m_ref, alpha, need, m_use, scale_log2);
+    } else if (i < 13) {
+      const int e = 2 * (i - 5);
+      w[e] = weight(w[e], scale_log2, m_use);
+      w[e + 1] = weight(w[e + 1], scale_log2, m_use);
+    }
+    if (i == 10) {
+      pb[0] = pack_weights(w, 0);
+      pin(pb[0]);
+    }
+    if (i == 14) {
+      pb[1] = pack_weights(w, 1);
+      pin(pb[1]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Phase 2: the 16 MFMAs of P.V for the current tile, beside the weights of keys 32..63 (slots 0-7), their bf16
+// rounding (slots 5, 9; each needed three slots later) and both row sums.
+template <int D>
+__device__ __forceinline__ void stage_phase2(const char* vc, f32x16 (&acc)[Geom<D>::CT], const LaneAddr<D>& la,
+                                             float (&w)[32], bf16x8 (&pb)[4], float alpha, float m_use,
+                                             float scale_log2, float& l_run, float& lq_run) {
+  using G = Geom<D>;
+  constexpr int NM = 4 * G::CT;
+  static_assert(NM == 16, "the slot plan below is laid out for 16 MFMAs per phase");
+  bf16x8 vf[3];
+  vf[0] = v_frag<D>(vc, la, 0);
+  vf[1] = v_frag<D>(vc, la, 1);
+  float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float q[2] = {0.0f, 0.0f};
+#pragma unroll
+  for (int j = 0; j < NM; ++j) {
+    if (j + 2 < NM) vf[(j + 2) % 3] = v_frag<D>(vc, la, j + 2);
+    acc[j % G::CT] = mfma(vf[j % 3], pb[j / G::CT], acc[j % G::CT]);
+    if (j < 8) {
+      const int e = 16 + 2 * j;
+      w[e] = weight(w[e], scale_log2, m_use);
+      w[e + 1] = weight(w[e + 1], scale_log2, m_use);
+      p[j & 3] += w[2 * j] + w[2 * j + 1];
+    } else {
+      p[j & 3] += w[2 * j] + w[2 * j + 1];
+    }
+    if (j == 5) pb[2] = pack_weights(w, 2);
+    if (j == 9) pb[3] = pack_weights(w, 3);
+    // bf16 sum, one pair per slot: pb[0] and pb[1] in slots 0-7, pb[2] in slots 8-11, pb[3] in slots 12-15
+    q[j & 1] = dot_pair(pb[j >> 2], j & 3, q[j & 1]);
+    pin(p[j & 3]);
+    pin(q[j & 1]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  l_run = __builtin_fmaf(alpha, l_run, (p[0] + p[1]) + (p[2] + p[3]));
+  lq_run = __builtin_fmaf(alpha, lq_run, q[0] + q[1]);
 }
 
 // Q^T fragment (B operand) of this wave's 32 rows starting at `row0` of the workgroup's block: lane holds row
@@ -291,8 +471,7 @@ __device__ __forceinline__ void decode_block(int n_qtiles, int xcd_remap, int64_
 }
 
 // ------------------------------------------------------------------------------------------------------------
-// The kernel: 4 waves, 128 query rows, one barrier per tile; the copy of tile t+1 is issued right after the
-// barrier of tile t into the slots tile t-1 left.
+// The kernel: 4 waves, 128 query rows, one barrier per pipeline stage.
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRows = 32 * kWaves;
@@ -301,6 +480,9 @@ constexpr int kRows = 32 * kWaves;
 // two workgroups of 64 KB LDS per CU), d = 64 ~135 (three), d = 24 ~90 (four).
 template <int D>
 constexpr int waves_per_simd() { return D >= 128 ? 2 : D >= 64 ? 3 : 4; }
+// The software pipeline keeps two score tiles live (32 more registers); it fits the d = 128 budget only.
+template <int D>
+constexpr bool pipelined() { return D == 128; }
 
 template <int D, bool OF32>
 __global__ __launch_bounds__(kThreads)
@@ -316,7 +498,10 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
   __shared__ __attribute__((aligned(1024))) char v0[T];
   __shared__ __attribute__((aligned(1024))) char v1[T];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  // the wave index is uniform across the wave; saying so keeps every per-wave bound (and the branches on them)
+  // in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int64_t bh;
   int qt;
   decode_block(n_qtiles, xcd_remap, bh, qt);
@@ -332,9 +517,14 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
   const int nfull = wkfull > 0 ? wkfull / kBN : 0;
   const int wkend = a.causal ? min(a.Nk, wrow0 + 31 + a.diag + 1) : a.Nk;
 
+  // tiles this wave has any visible key in (rows past Nq may see further; they are never stored)
+  const int nt_w = min(ntiles, wkend > 0 ? (wkend + kBN - 1) / kBN : 0);
+  constexpr bool kPipe = pipelined<D>();
+
   if (ntiles > 0) {
     issue_copy<D, true, kWaves>(K, 0, a.Nk, k0, wave, lane);
     issue_copy<D, false, kWaves>(V, 0, a.Nk, v0, wave, lane);
+    if (kPipe && ntiles > 1) issue_copy<D, true, kWaves>(K, kBN, a.Nk, k1, wave, lane);
   }
   bf16x8 qf[G::KSTEPS];
   load_q<D>(reinterpret_cast<const __bf16*>(a.q) + (bh * (int64_t)a.Nq + q0) * D, min(kRows, a.Nq - q0),
@@ -346,23 +536,81 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
 #pragma unroll
   for (int ct = 0; ct < G::CT; ++ct) acc[ct] = f32x16{};
   float m_ref = -INFINITY, l_run = 0.0f, lq_run = 0.0f;
-  auto step = [&](int t, const char* kc, const char* vc, char* kn, char* vn) {
-    wait_vmem_all();      // this wave's copies of tile t have landed
-    __syncthreads();      // every wave's copies have landed; every wave is done with tile t-1
-    if (t + 1 < ntiles) {
-      issue_copy<D, true, kWaves>(K, (t + 1) * kBN, a.Nk, kn, wave, lane);
-      issue_copy<D, false, kWaves>(V, (t + 1) * kBN, a.Nk, vn, wave, lane);
-    }
-    if (t * kBN >= wkend) return;
-    f32x16 s0, s1;
+
+  // One tile at a time (the last tile of a wave, tiles on the diagonal, and every tile when d < 128): scores,
+  // mask, weights, rescale, P.V, sums.
+  auto plain_tile = [&](const f32x16& c0, const f32x16& c1, bool partial, int t, const char* vc) {
+    float w[32];
     bf16x8 pb[4];
-    qk_tile<D>(kc, qf, s0, s1, la);
-    softmax_tile<D>(s0, s1, pb, acc, m_ref, l_run, lq_run, t >= nfull, row_lim - t * kBN, a.scale_log2);
-    pv_tile<D>(vc, pb, acc, la);
+    float alpha;
+    bool need;
+    unpack_scores(c0, c1, w);
+    if (partial) mask_tile(w, row_lim - t * kBN);
+    weights_tile(w, pb, m_ref, alpha, need, a.scale_log2);
+    rescale_acc<D>(acc, alpha, need);
+    __builtin_amdgcn_sched_barrier(0);
+    pv_tile<D, kPipe>(vc, pb, acc, la);
+    sums_tile(w, pb, alpha, l_run, lq_run);
   };
-  for (int t = 0; t < ntiles; t += 2) {
-    step(t, k0, v0, k1, v1);
-    if (t + 1 < ntiles) step(t + 1, k1, v1, k0, v0);
+
+  if constexpr (kPipe) {
+    // Software pipeline, one stage per tile t: the scores of tile t+1 (K tile t+1) are computed beside tile t's
+    // weights, then P.V of tile t (V tile t) beside the rest of tile t's softmax. K tiles therefore arrive one
+    // tile ahead of V tiles: after the barrier of stage t, K tile t+2 is copied into the slot of K tile t and V
+    // tile t+1 into the slot of V tile t-1.
+    f32x16 sa0, sa1, sb0, sb1;
+    wait_vmem_all();
+    __syncthreads();
+    if (nt_w > 0) qk_tile<D, true>(k0, qf, sa0, sa1, la);
+    auto stage = [&](int t, f32x16& c0, f32x16& c1, f32x16& n0, f32x16& n1, const char* kn, char* kw,
+                     const char* vc, char* vw) {
+      wait_vmem_all();      // this wave's copies of K tile t+1 and V tile t have landed
+      __syncthreads();      // so have every wave's; every wave is done with K tile t and V tile t-1
+      if (t + 2 < ntiles) issue_copy<D, true, kWaves>(K, (t + 2) * kBN, a.Nk, kw, wave, lane);
+      if (t + 1 < ntiles) issue_copy<D, false, kWaves>(V, (t + 1) * kBN, a.Nk, vw, wave, lane);
+      // A wave past its last visible tile writes zeros to n0/n1: every path then writes them, so the scores of
+      // tile t, which reach this stage in c0/c1, are dead once unpacked and are not kept beside their copy.
+      if (t >= nt_w) {
+        n0 = f32x16{};
+        n1 = f32x16{};
+        return;
+      }
+      float w[32];
+      bf16x8 pb[4];
+      float alpha, m_use;
+      bool need;
+      unpack_scores(c0, c1, w);
+      if (t >= nfull) mask_tile(w, row_lim - t * kBN);
+      // The wave's last tile computes the scores of one more tile, which are never used (K slot `kn` then holds
+      // an older tile): one branch-free stage shape keeps the register allocation of the loop tight.
+      __builtin_amdgcn_sched_barrier(0);
+      stage_phase1<D>(kn, qf, n0, n1, la, w, pb, m_ref, alpha, need, m_use, a.scale_log2);
+      rescale_acc<D>(acc, alpha, need);
+      __builtin_amdgcn_sched_barrier(0);
+      stage_phase2<D>(vc, acc, la, w, pb, alpha, m_use, a.scale_log2, l_run, lq_run);
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+      stage(t, sa0, sa1, sb0, sb1, k1, k0, v0, v1);
+      if (t + 1 < ntiles) stage(t + 1, sb0, sb1, sa0, sa1, k0, k1, v1, v0);
+    }
+  } else {
+    // One tile per step: after the barrier of tile t, tile t+1 is copied into the slots tile t-1 left.
+    auto step = [&](int t, const char* kc, const char* vc, char* kn, char* vn) {
+      wait_vmem_all();      // this wave's copies of tile t have landed
+      __syncthreads();      // every wave's copies have landed; every wave is done with tile t-1
+      if (t + 1 < ntiles) {
+        issue_copy<D, true, kWaves>(K, (t + 1) * kBN, a.Nk, kn, wave, lane);
+        issue_copy<D, false, kWaves>(V, (t + 1) * kBN, a.Nk, vn, wave, lane);
+      }
+      if (t >= nt_w) return;
+      f32x16 s0, s1;
+      qk_tile<D>(kc, qf, s0, s1, la);
+      plain_tile(s0, s1, t >= nfull, t, vc);
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+      step(t, k0, v0, k1, v1);
+      if (t + 1 < ntiles) step(t + 1, k1, v1, k0, v0);
+    }
   }
   store_out<D, OF32>(a, bh, q0, kRows, wave * 32 + (lane & 31), lane, acc, m_ref, l_run, lq_run);
 }
