@@ -123,8 +123,10 @@ int enqueue_fwd(const void* q, const void* k, const void* v, void* o, float* lse
   a.Nq = Nq;
   a.Nk = Nk;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
-  a.causal = causal;
-  a.diag = diag;
+  // a causal mask under which even the first query row sees every key hides nothing: run the unmasked kernel
+  const bool masks = causal && (int64_t)diag < (int64_t)Nk - 1;
+  a.causal = masks ? 1 : 0;
+  a.diag = masks ? diag : 0;
   if (in_dtype == ATTN_F32)
     e = ebattn::launch_attn_fwd_f32(a, d, stream);
   else if (Nq <= ebattn::kShortMax && Nk <= ebattn::kShortMax)

@@ -51,6 +51,7 @@ constexpr int kBN = 64;                        // keys per K/V tile
 constexpr int32_t kRsrcWord3 = 0x00020000;     // raw buffer, 32-bit data format (gfx9 family)
 constexpr uint32_t kOutOfRange = 0x7ffffff0u;  // a buffer offset past every num_records: the load returns 0
 constexpr float kRescaleSlack = 8.0f;          // log2 units the running maximum may exceed the reference by
+constexpr int kLead = 3;                       // LDS operand reads run this many MFMAs ahead (fenced loops)
 
 template <int D>
 struct Geom {
@@ -95,23 +96,39 @@ __device__ __forceinline__ float pair_sum(float x) {
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 // This wave's share (of NW waves) of the HBM -> LDS copy of tile rows [j0, j0 + kBN) of K (IS_K: rows permuted,
-// chunks K-swizzled) or of V (chunks V-swizzled). Rows past Nk read as zero.
+// chunks K-swizzled) or of V (chunks V-swizzled): kPerWave wave-wide copy instructions of 16 bytes per lane. Rows
+// past Nk read as zero (a tile wholly past Nk is all zeros and touches no memory).
 template <int D, bool IS_K, int NW>
-__device__ __forceinline__ void issue_copy(const __bf16* X, int j0, int Nk, char* dst, int wave, int lane) {
+struct TileCopy {
   using G = Geom<D>;
   static_assert(G::INSTR % NW == 0, "tile copy must split evenly over the waves");
-  const int rows_valid = min(kBN, Nk - j0);
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(X + (int64_t)j0 * D, (int64_t)rows_valid * D * 2);
-  const int sub = lane / G::CPR, pos = lane % G::CPR;
-#pragma unroll
-  for (int i = 0; i < G::INSTR / NW; ++i) {
-    const int instr = wave * (G::INSTR / NW) + i;
+  static constexpr int kPerWave = G::INSTR / NW;
+  __amdgpu_buffer_rsrc_t rx;
+  char* dst;
+  int wave, lane;
+  __device__ __forceinline__ TileCopy(const __bf16* X, int j0, int Nk, char* dst_, int wave_, int lane_)
+      : dst(dst_), wave(wave_), lane(lane_) {
+    const int rows_valid = min(kBN, Nk - j0);
+    rx = make_rsrc(X + (int64_t)j0 * D, (int64_t)rows_valid * D * 2);
+  }
+  __device__ __forceinline__ void issue(int i) const {
+    const int sub = lane / G::CPR, pos = lane % G::CPR;
+    const int instr = wave * kPerWave + i;
     const int row = instr * G::ROWS_PER_INSTR + sub;
     const int m = pos ^ (IS_K ? k_swz<D>(row) : v_swz<D>(row));
     const int src_row = IS_K ? key_of_row(row) : row;
     const uint32_t off = m < G::CPG ? (uint32_t)((src_row * D + m * 8) * 2) : kOutOfRange;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(dst + instr * 1024), 16, off, 0, 0, 0);
   }
+  __device__ __forceinline__ void issue_all() const {
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) issue(i);
+  }
+};
+
+template <int D, bool IS_K, int NW>
+__device__ __forceinline__ void issue_copy(const __bf16* X, int j0, int Nk, char* dst, int wave, int lane) {
+  TileCopy<D, IS_K, NW>(X, j0, Nk, dst, wave, lane).issue_all();
 }
 
 // Per-lane pieces of the LDS addressing, fixed for the whole key loop.
@@ -175,16 +192,16 @@ __device__ __forceinline__ void qk_tile(const char* kt, const bf16x8 (&qf)[Geom<
   using G = Geom<D>;
   if constexpr (FENCED) {
     constexpr int NM = 2 * G::KSTEPS;
-    bf16x8 kf[3];
-    kf[0] = k_frag<D>(kt, la, 0);
-    kf[1] = k_frag<D>(kt, la, 1);
+    bf16x8 kf[kLead + 1];
+#pragma unroll
+    for (int i = 0; i < kLead; ++i) kf[i] = k_frag<D>(kt, la, i);
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
-      if (i + 2 < NM) kf[(i + 2) % 3] = k_frag<D>(kt, la, i + 2);
+      if (i + kLead < NM) kf[(i + kLead) % (kLead + 1)] = k_frag<D>(kt, la, i + kLead);
       if (i & 1)
-        s1 = mfma(kf[i % 3], qf[i >> 1], i < 2 ? f32x16{} : s1);
+        s1 = mfma(kf[i % (kLead + 1)], qf[i >> 1], i < 2 ? f32x16{} : s1);
       else
-        s0 = mfma(kf[i % 3], qf[i >> 1], i < 2 ? f32x16{} : s0);
+        s0 = mfma(kf[i % (kLead + 1)], qf[i >> 1], i < 2 ? f32x16{} : s0);
       __builtin_amdgcn_sched_barrier(0);
     }
   } else {
@@ -217,13 +234,15 @@ __device__ __forceinline__ bf16x8 pack_weights(const float (&w)[32], int kk) {
   return __builtin_convertvector(v, bf16x8);
 }
 
-// Hides the keys of a tile that straddles the causal diagonal: keys past `lim` (relative to this lane's first
-// key of the tile) are hidden.
-__device__ __forceinline__ void mask_tile(float (&w)[32], int lim) {
+// Hides the keys of a tile that straddles the causal diagonal, in the score accumulators themselves (masking the
+// unpacked copy instead makes the allocator keep both): keys past `lim` (relative to this lane's first key of the
+// tile) are hidden.
+__device__ __forceinline__ void mask_scores(f32x16& s0, f32x16& s1, int lim) {
 #pragma unroll
-  for (int e = 0; e < 32; ++e) {
-    const int r = e & 15;
-    if (32 * (e >> 4) + 16 * (r >> 3) + (r & 7) > lim) w[e] = -INFINITY;
+  for (int r = 0; r < 16; ++r) {
+    const int kr = 16 * (r >> 3) + (r & 7);
+    if (kr > lim) s0[r] = -INFINITY;
+    if (kr + 32 > lim) s1[r] = -INFINITY;
   }
 }
 
@@ -303,13 +322,13 @@ __device__ __forceinline__ void pv_tile(const char* vt, const bf16x8 (&pb)[4], f
   using G = Geom<D>;
   constexpr int NM = 4 * G::CT;
   if constexpr (FENCED) {
-    bf16x8 vf[3];
-    vf[0] = v_frag<D>(vt, la, 0);
-    vf[1] = v_frag<D>(vt, la, 1);
+    bf16x8 vf[kLead + 1];
+#pragma unroll
+    for (int j = 0; j < kLead; ++j) vf[j] = v_frag<D>(vt, la, j);
 #pragma unroll
     for (int j = 0; j < NM; ++j) {
-      if (j + 2 < NM) vf[(j + 2) % 3] = v_frag<D>(vt, la, j + 2);
-      acc[j % G::CT] = mfma(vf[j % 3], pb[j / G::CT], acc[j % G::CT]);
+      if (j + kLead < NM) vf[(j + kLead) % (kLead + 1)] = v_frag<D>(vt, la, j + kLead);
+      acc[j % G::CT] = mfma(vf[j % (kLead + 1)], pb[j / G::CT], acc[j % G::CT]);
       __builtin_amdgcn_sched_barrier(0);
     }
   } else {
@@ -325,24 +344,34 @@ __device__ __forceinline__ void pv_tile(const char* vt, const bf16x8 (&pb)[4], f
 // of the current tile -- with a scheduling fence after every slot so that the compiler keeps that order.
 //
 // Phase 1: the 16 MFMAs of the next tile's scores, beside the current tile's row maximum (slots 0-3), reference
-// update (slot 4), the weights of keys 0..31 (slots 5-12) and their bf16 rounding (slots 10, 14).
-template <int D>
+// update (slot 4), the weights of keys 0..31 (slots 5-12) and their bf16 rounding (slots 10, 14); the even slots
+// also issue this wave's share of the copies of K tile t+2 and V tile t+1.
+template <int D, class CopyK, class CopyV>
 __device__ __forceinline__ void stage_phase1(const char* kn, const bf16x8 (&qf)[Geom<D>::KSTEPS], f32x16& n0,
                                              f32x16& n1, const LaneAddr<D>& la, float (&w)[32], bf16x8 (&pb)[4],
-                                             float& m_ref, float& alpha, bool& need, float& m_use, float scale_log2) {
+                                             float& m_ref, float& alpha, bool& need, float& m_use, float scale_log2,
+                                             const CopyK& ck, const CopyV& cv) {
   constexpr int NM = 2 * Geom<D>::KSTEPS;
   static_assert(NM == 16, "the slot plan below is laid out for 16 MFMAs per phase");
-  bf16x8 kf[3];
-  kf[0] = k_frag<D>(kn, la, 0);
-  kf[1] = k_frag<D>(kn, la, 1);
+  static_assert(CopyK::kPerWave <= 4 && CopyV::kPerWave <= 4, "one tile-copy instruction per even slot");
+  bf16x8 kf[kLead + 1];
+#pragma unroll
+  for (int i = 0; i < kLead; ++i) kf[i] = k_frag<D>(kn, la, i);
   float pm[4];
 #pragma unroll
   for (int i = 0; i < NM; ++i) {
-    if (i + 2 < NM) kf[(i + 2) % 3] = k_frag<D>(kn, la, i + 2);
+    if (i + kLead < NM) kf[(i + kLead) % (kLead + 1)] = k_frag<D>(kn, la, i + kLead);
     if (i & 1)
-      n1 = mfma(kf[i % 3], qf[i >> 1], i < 2 ? f32x16{} : n1);
+      n1 = mfma(kf[i % (kLead + 1)], qf[i >> 1], i < 2 ? f32x16{} : n1);
     else
-      n0 = mfma(kf[i % 3], qf[i >> 1], i < 2 ? f32x16{} : n0);
+      n0 = mfma(kf[i % (kLead + 1)], qf[i >> 1], i < 2 ? f32x16{} : n0);
+    // the copies for the next stages, spread out so that the memory pipeline never backs up into the wave
+    if ((i & 1) == 0) {
+      if (i < 2 * CopyK::kPerWave)
+        ck.issue(i >> 1);
+      else if (i >= 8 && i < 8 + 2 * CopyV::kPerWave)
+        cv.issue((i - 8) >> 1);
+    }
     if (i < 4) {
       // IEEE maximum (v_maximum3_f32): no NaN quieting of the MFMA results is needed before it.
       float m = __builtin_elementwise_maximum(w[8 * i], w[8 * i + 1]);
@@ -380,15 +409,15 @@ __device__ __forceinline__ void stage_phase2(const char* vc, f32x16 (&acc)[Geom<
   using G = Geom<D>;
   constexpr int NM = 4 * G::CT;
   static_assert(NM == 16, "the slot plan below is laid out for 16 MFMAs per phase");
-  bf16x8 vf[3];
-  vf[0] = v_frag<D>(vc, la, 0);
-  vf[1] = v_frag<D>(vc, la, 1);
+  bf16x8 vf[kLead + 1];
+#pragma unroll
+  for (int j = 0; j < kLead; ++j) vf[j] = v_frag<D>(vc, la, j);
   float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   float q[2] = {0.0f, 0.0f};
 #pragma unroll
   for (int j = 0; j < NM; ++j) {
-    if (j + 2 < NM) vf[(j + 2) % 3] = v_frag<D>(vc, la, j + 2);
-    acc[j % G::CT] = mfma(vf[j % 3], pb[j / G::CT], acc[j % G::CT]);
+    if (j + kLead < NM) vf[(j + kLead) % (kLead + 1)] = v_frag<D>(vc, la, j + kLead);
+    acc[j % G::CT] = mfma(vf[j % (kLead + 1)], pb[j / G::CT], acc[j % G::CT]);
     if (j < 8) {
       const int e = 16 + 2 * j;
       w[e] = weight(w[e], scale_log2, m_use);
@@ -471,10 +500,7 @@ __device__ __forceinline__ void decode_block(int n_qtiles, int xcd_remap, int64_
 }
 
 // ------------------------------------------------------------------------------------------------------------
-// The kernel: 4 waves, 128 query rows, one barrier per pipeline stage.
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kRows = 32 * kWaves;
+// The kernel: 32 query rows per wave, one barrier per pipeline stage.
 
 // Waves per SIMD the register budget allows (512 VGPRs per SIMD lane): d = 128 needs ~210 registers (two waves,
 // two workgroups of 64 KB LDS per CU), d = 64 ~135 (three), d = 24 ~90 (four).
@@ -483,13 +509,18 @@ constexpr int waves_per_simd() { return D >= 128 ? 2 : D >= 64 ? 3 : 4; }
 // The software pipeline keeps two score tiles live (32 more registers); it fits the d = 128 budget only.
 template <int D>
 constexpr bool pipelined() { return D == 128; }
+// Waves per workgroup (32 query rows each): 4 (128 rows, two workgroups per CU) or, for the pipelined kernel
+// without a causal mask, 8 (256 rows, one workgroup per CU: each K/V tile is copied into LDS once per 256 rows
+// instead of once per 128; under a causal mask the waves of such a block finish too unevenly for it to pay).
 
-template <int D, bool OF32>
-__global__ __launch_bounds__(kThreads)
+template <int D, bool OF32, int NW>
+__global__ __launch_bounds__(64 * NW)
 __attribute__((amdgpu_waves_per_eu(waves_per_simd<D>(), waves_per_simd<D>())))
 void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
   using G = Geom<D>;
   constexpr int T = G::TILE_BYTES;
+  constexpr int kWaves = NW;
+  constexpr int kRows = 32 * kWaves;
   // Four separate LDS arrays (K slots 0/1, V slots 0/1), always named at compile time: the compiler can then
   // tell that a tile copy in flight into one slot does not alias operand reads from another, and does not stall
   // those reads on the copy; the explicit vmcnt wait before each barrier orders the copies.
@@ -539,13 +570,13 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
 
   // One tile at a time (the last tile of a wave, tiles on the diagonal, and every tile when d < 128): scores,
   // mask, weights, rescale, P.V, sums.
-  auto plain_tile = [&](const f32x16& c0, const f32x16& c1, bool partial, int t, const char* vc) {
+  auto plain_tile = [&](f32x16& c0, f32x16& c1, bool partial, int t, const char* vc) {
     float w[32];
     bf16x8 pb[4];
     float alpha;
     bool need;
+    if (partial) mask_scores(c0, c1, row_lim - t * kBN);
     unpack_scores(c0, c1, w);
-    if (partial) mask_tile(w, row_lim - t * kBN);
     weights_tile(w, pb, m_ref, alpha, need, a.scale_log2);
     rescale_acc<D>(acc, alpha, need);
     __builtin_amdgcn_sched_barrier(0);
@@ -566,11 +597,15 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
                      const char* vc, char* vw) {
       wait_vmem_all();      // this wave's copies of K tile t+1 and V tile t have landed
       __syncthreads();      // so have every wave's; every wave is done with K tile t and V tile t-1
-      if (t + 2 < ntiles) issue_copy<D, true, kWaves>(K, (t + 2) * kBN, a.Nk, kw, wave, lane);
-      if (t + 1 < ntiles) issue_copy<D, false, kWaves>(V, (t + 1) * kBN, a.Nk, vw, wave, lane);
+      // K tile t+2 goes to the slot of K tile t, V tile t+1 to the slot of V tile t-1 (tiles past the end are
+      // copied as zeros, which keeps the stage free of branches; nothing reads them)
+      const TileCopy<D, true, kWaves> ck(K, (t + 2) * kBN, a.Nk, kw, wave, lane);
+      const TileCopy<D, false, kWaves> cv(V, (t + 1) * kBN, a.Nk, vw, wave, lane);
       // A wave past its last visible tile writes zeros to n0/n1: every path then writes them, so the scores of
       // tile t, which reach this stage in c0/c1, are dead once unpacked and are not kept beside their copy.
       if (t >= nt_w) {
+        ck.issue_all();
+        cv.issue_all();
         n0 = f32x16{};
         n1 = f32x16{};
         return;
@@ -579,12 +614,12 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
       bf16x8 pb[4];
       float alpha, m_use;
       bool need;
+      if (t >= nfull) mask_scores(c0, c1, row_lim - t * kBN);
       unpack_scores(c0, c1, w);
-      if (t >= nfull) mask_tile(w, row_lim - t * kBN);
       // The wave's last tile computes the scores of one more tile, which are never used (K slot `kn` then holds
       // an older tile): one branch-free stage shape keeps the register allocation of the loop tight.
       __builtin_amdgcn_sched_barrier(0);
-      stage_phase1<D>(kn, qf, n0, n1, la, w, pb, m_ref, alpha, need, m_use, a.scale_log2);
+      stage_phase1<D>(kn, qf, n0, n1, la, w, pb, m_ref, alpha, need, m_use, a.scale_log2, ck, cv);
       rescale_acc<D>(acc, alpha, need);
       __builtin_amdgcn_sched_barrier(0);
       stage_phase2<D>(vc, acc, la, w, pb, alpha, m_use, a.scale_log2, l_run, lq_run);
@@ -615,15 +650,24 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
   store_out<D, OF32>(a, bh, q0, kRows, wave * 32 + (lane & 31), lane, acc, m_ref, l_run, lq_run);
 }
 
-template <int D, bool OF32>
+template <int D, bool OF32, int NW>
 hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
+  constexpr int kRows = 32 * NW;
   const int n_qtiles = (a.Nq + kRows - 1) / kRows;
   const int64_t total = (int64_t)n_qtiles * a.BH;
   if (total > 0x7fffffff) return hipErrorInvalidConfiguration;
   const int remap = (total % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, OF32>), dim3((unsigned)total), dim3(kThreads), 0, stream, a,
-                     n_qtiles, remap);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, OF32, NW>), dim3((unsigned)total), dim3(64 * NW), 0, stream, a, n_qtiles,
+                     remap);
   return hipGetLastError();
+}
+
+template <int D, bool OF32>
+hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
+  if constexpr (pipelined<D>()) {
+    if (!a.causal) return launch_d<D, OF32, 8>(a, stream);
+  }
+  return launch_d<D, OF32, 4>(a, stream);
 }
 
 }  // namespace
