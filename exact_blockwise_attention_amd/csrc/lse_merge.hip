@@ -8,7 +8,8 @@
 // empty parts merge to (0, -inf).
 //
 // The kernel is HBM-bound: per row it reads two d-vectors and two scalars and writes one d-vector and one
-// scalar. Each lane moves one 16-byte vector; a row is served by a power-of-two group of lanes inside one
+// scalar, every byte once, so the d-vectors are read and written with non-temporal accesses (they are not
+// kept in the caches). Each lane moves one 16-byte vector; a row is served by a power-of-two group of lanes inside one
 // wave, so the scalar lse of a row is read by every lane of the group before any lane of the same wave
 // stores (this keeps in-place merges, lse aliasing lse_a, race-free).
 #include "internal.h"
@@ -30,14 +31,17 @@ template <>
 struct PartVec<true> {
   static constexpr int N = 4;
   typedef f32x4 F;
-  __device__ static F load(const void* p, int64_t off) { return *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p) + off); }
+  __device__ static F load(const void* p, int64_t off) {
+    return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p) + off));
+  }
 };
 template <>
 struct PartVec<false> {
   static constexpr int N = 8;
   typedef f32x8 F;
   __device__ static F load(const void* p, int64_t off) {
-    return __builtin_convertvector(*reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(p) + off), f32x8);
+    return __builtin_convertvector(
+        __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(p) + off)), f32x8);
   }
 };
 
@@ -74,12 +78,14 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(MergeArgs a) {
     if (OF32) {
       float* o = reinterpret_cast<float*>(a.o) + off;
 #pragma unroll
-      for (int q = 0; q < P::N; q += 4) *reinterpret_cast<f32x4*>(o + q) = f32x4{y[q], y[q + 1], y[q + 2], y[q + 3]};
+      for (int q = 0; q < P::N; q += 4)
+        __builtin_nontemporal_store(f32x4{y[q], y[q + 1], y[q + 2], y[q + 3]}, reinterpret_cast<f32x4*>(o + q));
     } else {
       __bf16* o = reinterpret_cast<__bf16*>(a.o) + off;
 #pragma unroll
       for (int q = 0; q < P::N; q += 4)
-        *reinterpret_cast<bf16x4*>(o + q) = __builtin_convertvector((f32x4{y[q], y[q + 1], y[q + 2], y[q + 3]}), bf16x4);
+        __builtin_nontemporal_store(__builtin_convertvector((f32x4{y[q], y[q + 1], y[q + 2], y[q + 3]}), bf16x4),
+                                    reinterpret_cast<bf16x4*>(o + q));
     }
   }
   if (c0 == 0) a.lse[row] = lse;
