@@ -1,6 +1,6 @@
 """Benchmark of the exact blockwise attention forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu] [--copy-probe BYTES]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu] [--copy-probe BYTES] [--merge-only]
 
 A step is one attention forward (scores, causal mask by position, online softmax, P.V, epilogue) over the
 causal self-attention workload B=4, H=32, N=8192, d=128, bf16 in / bf16 out with fp32 lse, inputs iid N(0,1)
@@ -107,12 +107,9 @@ def cpu_baseline(cfg, q_bits, k_bits, v_bits, budget_s=15.0):
                       f"(float64 numpy oracle, {elapsed:.1f} s); rate = 4*d*visible pairs / time"}
 
 
-def bench_extra(torch, eb, dev, steps):
-    """Merge bandwidth at the ring-share shape, and the ring-share / striped workloads end to end."""
-    from workloads import CONFIGS, normal_bf16_bits
+def bench_merge(torch, eb, dev, steps):
+    """LSE merge of fp32 partials in place at the ring-share shape: 32*32768 rows x d=128, 1.62 GB per launch."""
     from workloads import accounting as acc
-    out = {}
-    # LSE merge, fp32 partials in place: 32*32768 rows x d=128 (1.62 GB moved per launch)
     rows, d = 32 * 32768, 128
     g = torch.Generator(device=dev)
     g.manual_seed(3)
@@ -122,10 +119,15 @@ def bench_extra(torch, eb, dev, steps):
     lb = torch.randn((rows,), device=dev, generator=g)
     ms = time_region(torch, lambda: eb.attn_lse_merge(oa, la, ob, lb, out=oa, lse_out=la), max(steps, 10), 3)
     nbytes = acc.merge_bytes(rows, d, 4, 4)
-    out["lse_merge_f32_inplace_1M_rows_d128"] = {"ms": ms, "GB/s": nbytes / ms / 1e6,
-                                                 "frac_hbm_peak": nbytes / ms / 1e6 / PEAK_HBM_GBS,
-                                                 "bytes_per_launch": nbytes}
-    del oa, ob, la, lb
+    return {"ms": ms, "GB/s": nbytes / ms / 1e6, "frac_hbm_peak": nbytes / ms / 1e6 / PEAK_HBM_GBS,
+            "bytes_per_launch": nbytes}
+
+
+def bench_extra(torch, eb, dev, steps):
+    """Merge bandwidth at the ring-share shape, and the ring-share / striped workloads end to end."""
+    from workloads import CONFIGS, normal_bf16_bits
+    from workloads import accounting as acc
+    out = {"lse_merge_f32_inplace_1M_rows_d128": bench_merge(torch, eb, dev, steps)}
     # ring share, rank 2 of 4, global N = 131072
     c3 = CONFIGS["ring_rank2of4_128k"]
     n = c3.Nq
@@ -183,6 +185,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="also run one plain device copy of this many bytes (counter calibration)")
+    ap.add_argument("--merge-only", action="store_true",
+                    help="time only the LSE merge (for profiling it) and print its figures as one JSON line")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this build has no "
@@ -196,6 +200,17 @@ def main(argv=None):
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_probe > 0:
+        src = torch.empty(args.copy_probe // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: {src.numel() * 4} bytes read, {dst.numel() * 4} bytes written")
+        del src, dst
+    if args.merge_only:
+        print(json.dumps({"lse_merge_f32_inplace_1M_rows_d128": bench_merge(torch, eb, dev, args.steps)}), flush=True)
+        return 0
     cfg = CONFIGS["causal_8k"]
     t0 = time.perf_counter()
     q_bits = normal_bf16_bits(cfg.seed, "q", (cfg.B, cfg.H, cfg.Nq, cfg.d))
@@ -205,15 +220,6 @@ def main(argv=None):
     o = torch.empty_like(q)
     lse = torch.empty((cfg.B, cfg.H, cfg.Nq), dtype=torch.float32, device=dev)
     log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s")
-
-    if args.copy_probe > 0:
-        src = torch.empty(args.copy_probe // 4, dtype=torch.float32, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"[bench] copy probe: {src.numel() * 4} bytes read, {dst.numel() * 4} bytes written")
-        del src, dst
 
     def step():
         eb.attn_fwd(q, k, v, scale=cfg.scale, causal=True, out=o, lse=lse)
