@@ -11,8 +11,8 @@ seeded and already resident in HBM. The printed JSON line reports:
              launch from the committed rocprofv3 counter summary when it was taken on the current kernel
              source, else null;
   cpu_baseline  the float64 oracle timed on this host on a bounded row sample of the same workload;
-  extra      secondary measurements: the LSE merge at the ring-share shape (HBM-bound) and the ring-share /
-             striped workloads end to end.
+  extra      secondary measurements: the LSE merge at the ring-share shape (HBM-bound), the ring-share /
+             striped workloads end to end, and both axes of the tabular workload.
 """
 from __future__ import annotations
 
@@ -173,6 +173,34 @@ def bench_extra(torch, eb, dev, steps):
         fl = acc.attention_flops(acc.config_pairs(cr), cr.d)
         per_rank[f"r{r}"] = {"ms": ms, "TFLOP/s": fl / ms / 1e9, "frac_mfma_peak": fl / ms / 1e9 / PEAK_BF16_TFLOPS}
     out["striped_64k_ring_local"] = per_rank
+    del qd, kd, vd, blocks, o, lse, ws, Q, K, V
+    torch.cuda.empty_cache()
+    out.update(bench_tabular(torch, eb, dev, steps))
+    return out
+
+
+def bench_tabular(torch, eb, dev, steps):
+    """The tabular stand-in, both axes of one (1, 150000, 8, 4, 24) tensor: the row axis (8*4 sequences of
+    150000 tokens, d = 24, bound by the exponential and vector ALU work) and the feature axis (600000 sequences of
+    8 tokens, HBM-bound). The permutation between the two layouts happens outside the timed region."""
+    from workloads import CONFIGS, normal_bf16_bits
+    from workloads import accounting as acc
+    cr = CONFIGS["tabular_rows_150k"]
+    q, k, v = (upload_bf16(normal_bf16_bits(cr.seed, t, (cr.B, cr.H, cr.Nq, cr.d)), torch, dev) for t in "qkv")
+    o = torch.empty_like(q)
+    lse = torch.empty((cr.B, cr.H, cr.Nq), dtype=torch.float32, device=dev)
+    ms = time_region(torch, lambda: eb.attn_fwd(q, k, v, scale=cr.scale, out=o, lse=lse), max(2, steps // 4), 1)
+    fl = acc.attention_flops(acc.config_pairs(cr), cr.d)
+    out = {"tabular_rows_150k_d24": {"ms": ms, "TFLOP/s": fl / ms / 1e9, "frac_mfma_peak": fl / ms / 1e9 / PEAK_BF16_TFLOPS}}
+    cf = CONFIGS["tabular_features_8"]
+    qf, kf, vf = (x.permute(2, 1, 0, 3).contiguous() for x in (q, k, v))   # -> [rows, heads, features, d]
+    del q, k, v, o, lse
+    of = torch.empty_like(qf)
+    lf = torch.empty((cf.B, cf.H, cf.Nq), dtype=torch.float32, device=dev)
+    ms = time_region(torch, lambda: eb.attn_fwd(qf, kf, vf, scale=cf.scale, out=of, lse=lf), max(steps, 10), 3)
+    nbytes = acc.attn_fwd_bytes(cf.B, cf.H, cf.Nq, cf.Nq, cf.d, 2, 2)
+    out["tabular_features_8_d24"] = {"ms": ms, "GB/s": nbytes / ms / 1e6, "frac_hbm_peak": nbytes / ms / 1e6 / PEAK_HBM_GBS,
+                                     "bytes_per_launch": nbytes}
     return out
 
 

@@ -28,26 +28,34 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_short_kernel(FwdArgs a, int
   const int64_t bh0 = (int64_t)blockIdx.x * seqs_per_wg;
   const int nseq = (int)min<int64_t>(seqs_per_wg, a.BH - bh0);
 
+  // This lane's query row is loaded first, so that its latency overlaps the staging of K and V. K and V are
+  // streamed once, with non-temporal loads (the 48-byte query and output rows of neighbouring lanes share cache
+  // lines, so those accesses stay ordinary).
+  const int s = tid / a.Nq, i = tid % a.Nq;
+  const bool live = s < nseq;
+  const int64_t bh = bh0 + (live ? s : 0);
+  const __bf16* qrow = reinterpret_cast<const __bf16*>(a.q) + (bh * a.Nq + (live ? i : 0)) * D;
+  bf16x8 qv[D / 8];
+#pragma unroll
+  for (int c = 0; c < D / 8; ++c) qv[c] = reinterpret_cast<const bf16x8*>(qrow)[c];
+
   // Stage K and V of this workgroup's slices (contiguous) in LDS.
   const int chunks = nseq * a.Nk * (D / 8);
   const u32x4* Kg = reinterpret_cast<const u32x4*>(reinterpret_cast<const __bf16*>(a.k) + bh0 * a.Nk * D);
   const u32x4* Vg = reinterpret_cast<const u32x4*>(reinterpret_cast<const __bf16*>(a.v) + bh0 * a.Nk * D);
   for (int e = tid; e < chunks; e += kThreads) {
-    reinterpret_cast<u32x4*>(Kl)[e] = Kg[e];
-    reinterpret_cast<u32x4*>(Vl)[e] = Vg[e];
+    reinterpret_cast<u32x4*>(Kl)[e] = __builtin_nontemporal_load(Kg + e);
+    reinterpret_cast<u32x4*>(Vl)[e] = __builtin_nontemporal_load(Vg + e);
   }
   __syncthreads();
+  if (!live) return;
 
-  const int s = tid / a.Nq, i = tid % a.Nq;
-  if (s >= nseq) return;
-  const int64_t bh = bh0 + s;
-  const __bf16* qrow = reinterpret_cast<const __bf16*>(a.q) + (bh * a.Nq + i) * D;
   float q[D];
 #pragma unroll
-  for (int c = 0; c < D; c += 8) {
-    const f32x8 x = __builtin_convertvector(*reinterpret_cast<const bf16x8*>(qrow + c), f32x8);
+  for (int c = 0; c < D / 8; ++c) {
+    const f32x8 x = __builtin_convertvector(qv[c], f32x8);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) q[c + e] = x[e];
+    for (int e = 0; e < 8; ++e) q[8 * c + e] = x[e];
   }
   const __bf16* Ks = Kl + (int64_t)s * a.Nk * D;
   const __bf16* Vs = Vl + (int64_t)s * a.Nk * D;
@@ -97,8 +105,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_short_kernel(FwdArgs a, int
     if (OF32)
       *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.o) + (bh * a.Nq + i) * D + c) = y;
     else
-      *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(a.o) + (bh * a.Nq + i) * D + c) =
-          __builtin_convertvector(y, bf16x4);
+      *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(a.o) + (bh * a.Nq + i) * D + c) = __builtin_convertvector(y, bf16x4);
   }
 }
 
