@@ -22,12 +22,15 @@
 //   * the reference maximum only moves when a row's new maximum exceeds it by more than 8 (log2 units), so most
 //     tiles skip the rescale of the accumulator; the weights stay below 2^8 and the result is unchanged (the
 //     final normalisation uses the same reference).
+//   * at d = 128 the key loop is software-pipelined: while the MFMAs of the next tile's scores run, the wave
+//     forms the current tile's weights, and while the current tile's P.V MFMAs run, it finishes the weights and
+//     the row sums (the stage functions below lay this out slot by slot).
 // Per workgroup:
 //   * 64-key K and V tiles are copied HBM -> LDS by the buffer unit itself (buffer_load ... lds, 16 bytes per
 //     lane, rows past Nk read as zero), double-buffered in four separately named LDS arrays; K rows and V rows
 //     are XOR-swizzled per 16-byte chunk so that the operand reads spread over all 64 LDS banks;
-//   * 4 waves = 128 query rows per workgroup, one barrier per tile; two workgroups share a CU (d = 64, 128),
-//     so on each SIMD one wave's softmax can overlap the other's MFMA work.
+//   * 4 waves = 128 query rows per workgroup (8 waves = 256 rows for unmasked d = 128 calls), one barrier per
+//     tile; two waves share each SIMD, so one wave's softmax can also overlap the other's MFMA work.
 #include <type_traits>
 
 #include "internal.h"
@@ -619,7 +622,11 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
       // The wave's last tile computes the scores of one more tile, which are never used (K slot `kn` then holds
       // an older tile): one branch-free stage shape keeps the register allocation of the loop tight.
       __builtin_amdgcn_sched_barrier(0);
+      // Raised wave priority for phase 1: its chain (row maximum -> reference -> weights) gates the next phase,
+      // so the issue arbiter favours it over the SIMD's other wave (measured: +2.5 % causal, +0.7 % unmasked).
+      __builtin_amdgcn_s_setprio(1);
       stage_phase1<D>(kn, qf, n0, n1, la, w, pb, m_ref, alpha, need, m_use, a.scale_log2, ck, cv);
+      __builtin_amdgcn_s_setprio(0);
       rescale_acc<D>(acc, alpha, need);
       __builtin_amdgcn_sched_barrier(0);
       stage_phase2<D>(vc, acc, la, w, pb, alpha, m_use, a.scale_log2, l_run, lq_run);
