@@ -6,7 +6,7 @@
 // one slice onto MFMA would waste almost all of it, and the job is HBM-bound anyway, so a workgroup takes
 // many consecutive slices at once: it copies their K and V (contiguous in memory) into LDS with 16-byte
 // coalesced loads, then every lane computes one query row exactly (all scores, max, exp, sum, weighted
-// sum of V) in fp32.
+// sum of V) with fp32 arithmetic; the scores take the bf16 products in pairs (packed dot, fp32 sum).
 #include "internal.h"
 
 namespace ebattn {
@@ -17,6 +17,7 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 constexpr int kThreads = 256;
 
 template <int D, bool OF32>
@@ -50,31 +51,33 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_short_kernel(FwdArgs a, int
   __syncthreads();
   if (!live) return;
 
-  float q[D];
-#pragma unroll
-  for (int c = 0; c < D / 8; ++c) {
-    const f32x8 x = __builtin_convertvector(qv[c], f32x8);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) q[8 * c + e] = x[e];
-  }
+
   const __bf16* Ks = Kl + (int64_t)s * a.Nk * D;
   const __bf16* Vs = Vl + (int64_t)s * a.Nk * D;
   const int lim = a.causal ? min(i + a.diag, a.Nk - 1) : a.Nk - 1;   // last visible key of this row
 
+  // Scores with packed bf16 dot products (v_dot2_f32_bf16: two exact bf16 products added in fp32), two
+  // accumulators per key for a shorter dependency chain.
   float sc[kShortMax];
   float mx = -INFINITY;
 #pragma unroll
   for (int j = 0; j < kShortMax; ++j) {
     sc[j] = -INFINITY;
     if (j <= lim) {
-      float dot = 0.0f;
+      float d0 = 0.0f, d1 = 0.0f;
 #pragma unroll
-      for (int c = 0; c < D; c += 8) {
-        const f32x8 kx = __builtin_convertvector(*reinterpret_cast<const bf16x8*>(Ks + j * D + c), f32x8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dot = __builtin_fmaf(q[c + e], kx[e], dot);
+      for (int c = 0; c < D / 8; ++c) {
+        const bf16x8 kx = *reinterpret_cast<const bf16x8*>(Ks + j * D + 8 * c);
+        d0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(qv[c], qv[c], 0, 1),
+                                             __builtin_shufflevector(kx, kx, 0, 1), d0, false);
+        d1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(qv[c], qv[c], 2, 3),
+                                             __builtin_shufflevector(kx, kx, 2, 3), d1, false);
+        d0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(qv[c], qv[c], 4, 5),
+                                             __builtin_shufflevector(kx, kx, 4, 5), d0, false);
+        d1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(qv[c], qv[c], 6, 7),
+                                             __builtin_shufflevector(kx, kx, 6, 7), d1, false);
       }
-      sc[j] = dot * a.scale_log2;
+      sc[j] = (d0 + d1) * a.scale_log2;
       mx = fmaxf(mx, sc[j]);
     }
   }
