@@ -33,7 +33,9 @@
  *             gives such a part zero weight.
  *   Dtypes    ATTN_BF16 inputs run on bf16 MFMA with fp32 accumulation and fp32 softmax statistics
  *             ("深度学习注意力机制优化与FlashAttention实践" §5.1 advises fp32 for the statistics); the softmax
- *             weights P are rounded to bf16 before the P.V product. ATTN_F32 inputs run in fp32 throughout.
+ *             weights P are rounded to bf16 before the P.V product, and o is normalised by the sum of those
+ *             rounded weights (a constant V comes back exactly), while lse uses the sum of the fp32 weights.
+ *             ATTN_F32 inputs run in fp32 throughout.
  *   Asynchrony Every call only enqueues work on `stream`; nothing synchronises the device.
  *   Errors    Return ATTN_OK (0) or a negative code. Argument errors are detected before anything is
  *             launched; attn_last_error() then holds a message (thread-local). Launch failures return
