@@ -15,6 +15,9 @@ Sources (page title, then the section on it):
   [E] "注意力机制演进", timeline table, row "Striped Attention" (named only; defined here by position).
   [F] "Mosaic多轴注意力分片：突破Transformer长序列处理瓶颈", §3.2 -- after all K/V shards have passed, each device
       holds the complete attention output of its own query shard.
+  [G] "架构层解决方案 - Sparse Attention与Ring Attention", sections "Sliding Window Attention" (each token attends
+      only to the w most recent tokens) and "MQA与GQA" (query heads split into g groups, each group sharing one
+      key/value head; g = number of heads is plain multi-head attention, g = 1 is MQA).
 
 Readings where the pages are silent or garbled (each also listed in the design notes):
   * lse is the natural log of the sum of exp(scale * q.k) over the visible keys; no additive bias.
@@ -26,6 +29,11 @@ Readings where the pages are silent or garbled (each also listed in the design n
   * A query row with no visible key gets o = 0 and lse = -inf (no epsilon in the denominator); the merge treats
     lse = -inf as weight zero.
   * The scale is an explicit argument (the workloads pass 1/sqrt(d)).
+  * Sliding window ([G]): with a window of w positions a key is visible iff q_pos - w < k_pos <= q_pos, i.e. the w
+    most recent positions up to and including the query's own; a window is only defined together with the causal
+    mask. w = 0 means no window.
+  * Grouped-query attention ([G]): with Hkv key/value heads (Hkv divides H) query head h reads key/value head
+    h // (H // Hkv), so consecutive query heads share a key/value head, as in the section's figure.
 
 The attention here is the definition, not a blockwise algorithm: each query row's scores over ALL keys are
 materialised at once (rows are processed in chunks only to bound memory), so this code shares no structure with
@@ -39,17 +47,23 @@ _CHUNK_ELEMS = 8 << 20   # at most ~64 MB of float64 scores per chunk
 
 
 def visible(nq: int, nk: int, causal: bool, q_off: int = 0, k_off: int = 0, stride: int = 1,
-            rows=None) -> np.ndarray:
-    """Boolean [R, nk]: True where key j is visible to query row i ([D], [E] and the position reading above).
+            rows=None, window: int = 0) -> np.ndarray:
+    """Boolean [R, nk]: True where key j is visible to query row i ([D], [E], [G] and the readings above).
 
-    rows: optional query row indices (default: all nq rows).
+    rows: optional query row indices (default: all nq rows). window: sliding window in positions (0 = none;
+    requires causal).
     """
     r = np.arange(nq, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    if window and not causal:
+        raise ValueError("a sliding window is defined only with the causal mask")
     if not causal:
         return np.ones((r.size, nk), dtype=bool)
     q_pos = int(q_off) + int(stride) * r
     k_pos = int(k_off) + int(stride) * np.arange(nk, dtype=np.int64)
-    return k_pos[None, :] <= q_pos[:, None]
+    vis = k_pos[None, :] <= q_pos[:, None]
+    if window:
+        vis &= k_pos[None, :] > q_pos[:, None] - int(window)
+    return vis
 
 
 def _softmax_rows(s: np.ndarray, vis: np.ndarray):
@@ -67,21 +81,24 @@ def _softmax_rows(s: np.ndarray, vis: np.ndarray):
 
 
 def attention(q, k, v, scale: float, causal: bool = False, q_off: int = 0, k_off: int = 0, stride: int = 1,
-              rows=None):
+              rows=None, window: int = 0):
     """Exact attention ([A]) with the mask by global position, in float64.
 
-    q: [B, H, Nq, d]; k: [B, H, Nk, d]; v: [B, H, Nk, dv] (any real dtype; widened to float64).
+    q: [B, H, Nq, d]; k: [B, Hkv, Nk, d]; v: [B, Hkv, Nk, dv] (any real dtype; widened to float64), Hkv dividing
+       H (Hkv = H: multi-head; fewer: grouped-query, [G]).
     rows: optional 1-D indices of the query rows to compute (the same rows for every batch and head). Every
           output row depends only on its own query row and all keys, so a subset is exact.
+    window: sliding window in positions (0 = none), with causal only ([G]).
     Returns (o [B, H, R, dv] float64, lse [B, H, R] float64), lse in natural log.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     B, H, Nq, d = q.shape
-    Nk = k.shape[2]
-    if k.shape[:2] != (B, H) or v.shape[:3] != (B, H, Nk) or k.shape[3] != d:
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if (k.shape[0] != B or Hkv < 1 or H % Hkv != 0 or v.shape[:3] != (B, Hkv, Nk) or k.shape[3] != d):
         raise ValueError("shape mismatch")
+    group = H // Hkv
     rows = np.arange(Nq, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
     R = rows.size
     o = np.zeros((B, H, R, v.shape[3]), dtype=np.float64)
@@ -89,12 +106,13 @@ def attention(q, k, v, scale: float, causal: bool = False, q_off: int = 0, k_off
     chunk = max(1, _CHUNK_ELEMS // max(1, Nk))
     for c0 in range(0, R, chunk):
         rr = rows[c0:c0 + chunk]
-        vis = visible(Nq, Nk, causal, q_off, k_off, stride, rows=rr)
+        vis = visible(Nq, Nk, causal, q_off, k_off, stride, rows=rr, window=window)
         for b in range(B):
             for h in range(H):
-                s = scale * (q[b, h, rr] @ k[b, h].T)       # [r, Nk] scores, scaled ([A])
+                g = h // group                              # the key/value head of query head h ([G])
+                s = scale * (q[b, h, rr] @ k[b, g].T)       # [r, Nk] scores, scaled ([A])
                 p, l = _softmax_rows(s, vis)
-                o[b, h, c0:c0 + rr.size] = p @ v[b, h]
+                o[b, h, c0:c0 + rr.size] = p @ v[b, g]
                 lse[b, h, c0:c0 + rr.size] = l
     return o, lse
 
