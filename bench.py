@@ -12,7 +12,8 @@ seeded and already resident in HBM. The printed JSON line reports:
              source, else null;
   cpu_baseline  the float64 oracle timed on this host on a bounded row sample of the same workload;
   extra      secondary measurements: the LSE merge at the ring-share shape (HBM-bound), the ring-share /
-             striped workloads end to end, and both axes of the tabular workload.
+             striped workloads end to end, both axes of the tabular workload, and a sliding-window
+             grouped-query shape (attn_fwd_ex).
 """
 from __future__ import annotations
 
@@ -176,7 +177,27 @@ def bench_extra(torch, eb, dev, steps):
     del qd, kd, vd, blocks, o, lse, ws, Q, K, V
     torch.cuda.empty_cache()
     out.update(bench_tabular(torch, eb, dev, steps))
+    torch.cuda.empty_cache()
+    out.update(bench_window_gqa(torch, eb, dev, steps))
     return out
+
+
+def bench_window_gqa(torch, eb, dev, steps):
+    """attn_fwd_ex on a sliding-window, grouped-query shape of the kind the Sliding Window Attention and MQA/GQA
+    sections describe (a 4096-token window; 32 query heads sharing 8 key/value heads): causal self-attention
+    B=1, N=32768, d=128, bf16."""
+    from workloads import normal_bf16_bits
+    from workloads import accounting as acc
+    B, H, Hkv, N, d, w = 1, 32, 8, 32768, 128, 4096
+    q = upload_bf16(normal_bf16_bits(7, "q", (B, H, N, d)), torch, dev)
+    k = upload_bf16(normal_bf16_bits(7, "k", (B, Hkv, N, d)), torch, dev)
+    v = upload_bf16(normal_bf16_bits(7, "v", (B, Hkv, N, d)), torch, dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    ms = time_region(torch, lambda: eb.attn_fwd_ex(q, k, v, causal=True, window=w, out=o, lse=lse), max(steps, 10), 3)
+    fl = acc.attention_flops(B * H * acc.visible_pairs(N, N, True, window=w), d)
+    return {"swa4096_gqa32q8kv_32k_d128": {"ms": ms, "TFLOP/s": fl / ms / 1e9,
+                                          "frac_mfma_peak": fl / ms / 1e9 / PEAK_BF16_TFLOPS}}
 
 
 def bench_tabular(torch, eb, dev, steps):

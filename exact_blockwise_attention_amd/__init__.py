@@ -62,6 +62,8 @@ def _load() -> ctypes.CDLL:
     P, I, I64, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     lib.attn_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I64, I64, I, I, I, P]
     lib.attn_fwd.restype = I
+    lib.attn_fwd_ex.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, I, I64, I64, I, I64, I, I, P]
+    lib.attn_fwd_ex.restype = I
     lib.attn_lse_merge.argtypes = [P, P, P, P, P, P, I64, I, I, I, P]
     lib.attn_lse_merge.restype = I
     lib.ring_local.argtypes = [P, ctypes.POINTER(KVBlock), I, P, P, I, I, I, I, F, I, I64, I, I, I, P, SZ, P]
@@ -162,6 +164,35 @@ def attn_fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False, q_
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     _check(lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, d, scale, int(causal),
                         int(q_off), int(k_off), int(pos_stride), _code(q.dtype), _code(out.dtype), _stream(q)))
+    return out, lse
+
+
+def attn_fwd_ex(q, k, v, *, scale: Optional[float] = None, causal: bool = False, q_off: int = 0, k_off: int = 0,
+                pos_stride: int = 1, window: int = 0, out=None, lse=None, out_dtype=None) -> Tuple[object, object]:
+    """attn_fwd with grouped-query heads and a sliding window: q [B,H,Nq,d], k, v [B,Hkv,Nk,d] with Hkv dividing H
+    (query head h reads key/value head h // (H // Hkv)); window > 0 keeps, for each query, the keys of the
+    window most recent positions up to its own (causal only). Returns (o [B,H,Nq,d], lse [B,H,Nq] fp32)."""
+    torch = _torch()
+    _need_cuda(q, k, v, out, lse)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Hkv, Nk, d) or tuple(v.shape) != (B, Hkv, Nk, d):
+        raise ValueError("k and v must be [B, Hkv, Nk, d] with q's B and d")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share a dtype")
+    out_dtype = out_dtype or (out.dtype if out is not None else q.dtype)
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if tuple(out.shape) != (B, H, Nq, d) or tuple(lse.shape) != (B, H, Nq) or lse.dtype != torch.float32:
+        raise ValueError("out must be [B,H,Nq,d] and lse fp32 [B,H,Nq]")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _check(lib.attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Hkv, Nq, Nk, d, scale,
+                           int(causal), int(q_off), int(k_off), int(pos_stride), int(window), _code(q.dtype),
+                           _code(out.dtype), _stream(q)))
     return out, lse
 
 

@@ -53,6 +53,19 @@ int diag_offset(int64_t q_off, int64_t k_off, int s) {
   return (int)dq;
 }
 
+// With a sliding window of w positions, key j is also required to satisfy k_off + j*s > q_off + i*s - w, i.e.
+// j >= i + floor((q_off - k_off - w) / s) + 1. Clamped like diag_offset.
+int window_lo(int64_t q_off, int64_t k_off, int s, int64_t window) {
+  if (window <= 0) return ebattn::kNoWindow;
+  const int64_t num = q_off - k_off - window;
+  int64_t dq = num / s;
+  if ((num % s != 0) && (num < 0)) dq -= 1;  // floor division
+  const int64_t lim = (int64_t)1 << 29;
+  if (dq > lim) dq = lim;
+  if (dq < -lim) dq = -lim;
+  return (int)dq + 1;
+}
+
 const int64_t kOffLimit = (int64_t)1 << 62;
 
 // Common validation of a query-side call. Returns ATTN_OK or an error code (message set).
@@ -76,8 +89,9 @@ int check_query_side(const void* q, const void* o, const float* lse, int B, int 
   return ATTN_OK;
 }
 
+// BH: key/value slices (B * Hkv); BHq: query slices (B * H), which size o and lse.
 int check_kv(const void* k, const void* v, int64_t BH, int Nk, int d, int in_dtype, int64_t k_off,
-             const void* q, const void* o, const float* lse, int64_t Nq, int o_dtype) {
+             const void* q, const void* o, const float* lse, int64_t Nq, int o_dtype, int64_t BHq) {
   if (Nk < 0) return fail(ATTN_EINVAL, "negative Nk=%d", Nk);
   if (Nk > ATTN_MAX_SEQ) return fail(ATTN_EINVAL, "Nk=%d exceeds ATTN_MAX_SEQ", Nk);
   if (k_off > kOffLimit || k_off < -kOffLimit) return fail(ATTN_EINVAL, "k_off out of range");
@@ -85,7 +99,7 @@ int check_kv(const void* k, const void* v, int64_t BH, int Nk, int d, int in_dty
   if (!k || !v) return fail(ATTN_EINVAL, "null k or v pointer");
   if (!aligned(k, 16) || !aligned(v, 16)) return fail(ATTN_EINVAL, "k and v must be 16-byte aligned");
   const int64_t kvb = BH * Nk * d * elem_bytes(in_dtype);
-  const Span so = span(o, BH * Nq * d * elem_bytes(o_dtype)), sl = span(lse, BH * Nq * 4);
+  const Span so = span(o, BHq * Nq * d * elem_bytes(o_dtype)), sl = span(lse, BHq * Nq * 4);
   if (overlap(so, span(k, kvb)) || overlap(so, span(v, kvb)) || overlap(sl, span(k, kvb)) ||
       overlap(sl, span(v, kvb)))
     return fail(ATTN_EINVAL, "o/lse overlap k or v");
@@ -104,7 +118,8 @@ int check_outputs_disjoint(const void* q, const void* o, const float* lse, int64
 
 // Enqueue one attention forward whose arguments have been validated.
 int enqueue_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t BH, int Nq, int Nk,
-                int d, float scale, int causal, int diag, int in_dtype, int o_dtype, hipStream_t stream) {
+                int d, float scale, int causal, int diag, int in_dtype, int o_dtype, hipStream_t stream,
+                int lo = ebattn::kNoWindow, int kv_group = 1) {
   const int64_t rows = BH * Nq;
   if (rows == 0) return ATTN_OK;
   const bool all_hidden = (Nk == 0) || (causal && (int64_t)Nq - 1 + diag < 0);
@@ -123,10 +138,13 @@ int enqueue_fwd(const void* q, const void* k, const void* v, void* o, float* lse
   a.Nq = Nq;
   a.Nk = Nk;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
-  // a causal mask under which even the first query row sees every key hides nothing: run the unmasked kernel
-  const bool masks = causal && (int64_t)diag < (int64_t)Nk - 1;
+  // a causal mask under which even the first query row sees every key (and the last row's window reaches back
+  // to key 0) hides nothing: run the unmasked kernel
+  const bool masks = causal && ((int64_t)diag < (int64_t)Nk - 1 || (int64_t)Nq - 1 + lo > 0);
   a.causal = masks ? 1 : 0;
   a.diag = masks ? diag : 0;
+  a.lo = masks ? lo : ebattn::kNoWindow;
+  a.kv_group = kv_group;
   if (in_dtype == ATTN_F32)
     e = ebattn::launch_attn_fwd_f32(a, d, stream);
   else if (Nq <= ebattn::kShortMax && Nk <= ebattn::kShortMax)
@@ -155,21 +173,35 @@ const char* attn_last_error(void) { return g_err; }
 
 int attn_version(void) { return 100; }
 
-int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk, int d,
-             float scale, int causal, int64_t q_off, int64_t k_off, int pos_stride, int in_dtype, int o_dtype,
-             void* stream) {
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int Nq,
+                int Nk, int d, float scale, int causal, int64_t q_off, int64_t k_off, int pos_stride, int64_t window,
+                int in_dtype, int o_dtype, void* stream) {
   g_err[0] = '\0';
   int rc = check_query_side(q, o, lse, B, H, Nq, d, scale, causal, q_off, pos_stride, in_dtype, o_dtype);
   if (rc != ATTN_OK) return rc;
+  if (H > 0 && (Hkv < 1 || Hkv > H || H % Hkv != 0))
+    return fail(ATTN_EINVAL, "Hkv=%d must divide H=%d", Hkv, H);
+  if (window < 0) return fail(ATTN_EINVAL, "window must be >= 0 (got %lld)", (long long)window);
+  if (window > 0 && !causal) return fail(ATTN_EINVAL, "a sliding window requires causal = 1");
+  if (window > kOffLimit) return fail(ATTN_EINVAL, "window out of range");
   const int64_t BH = (int64_t)B * H;
-  rc = check_kv(k, v, BH, Nk, d, in_dtype, k_off, q, o, lse, Nq, o_dtype);
+  const int group = H > 0 ? H / Hkv : 1;
+  rc = check_kv(k, v, (int64_t)B * (H > 0 ? Hkv : 0), Nk, d, in_dtype, k_off, q, o, lse, Nq, o_dtype, BH);
   if (rc != ATTN_OK) return rc;
   if (BH * Nq == 0) return ATTN_OK;
   rc = check_outputs_disjoint(q, o, lse, BH * Nq, d, in_dtype, o_dtype);
   if (rc != ATTN_OK) return rc;
   (void)hipGetLastError();  // drop a stale error so a failure below is attributed to this call
   return enqueue_fwd(q, k, v, o, lse, BH, Nq, Nk, d, scale, causal, diag_offset(q_off, k_off, pos_stride),
-                     in_dtype, o_dtype, reinterpret_cast<hipStream_t>(stream));
+                     in_dtype, o_dtype, reinterpret_cast<hipStream_t>(stream),
+                     window_lo(q_off, k_off, pos_stride, window), group);
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk, int d,
+             float scale, int causal, int64_t q_off, int64_t k_off, int pos_stride, int in_dtype, int o_dtype,
+             void* stream) {
+  return attn_fwd_ex(q, k, v, o, lse, B, H, H, Nq, Nk, d, scale, causal, q_off, k_off, pos_stride, 0, in_dtype,
+                     o_dtype, stream);
 }
 
 int attn_lse_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b, void* o, float* lse,
@@ -250,7 +282,7 @@ int ring_local(const void* q_shard, const attn_kv_block* kv_blocks, int n_blocks
   const int64_t rows = BH * Nq;
   for (int i = 0; i < n_blocks; ++i) {
     rc = check_kv(kv_blocks[i].k, kv_blocks[i].v, BH, kv_blocks[i].Nk, d, in_dtype, kv_blocks[i].k_off, q_shard, o,
-                  lse, Nq, o_dtype);
+                  lse, Nq, o_dtype, BH);
     if (rc != ATTN_OK) {
       char msg[512];
       snprintf(msg, sizeof(msg), "block %d: %s", i, g_err);

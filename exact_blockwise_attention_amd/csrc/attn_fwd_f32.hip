@@ -23,8 +23,9 @@ __global__ __launch_bounds__(kRows) void attn_fwd_f32_kernel(FwdArgs a, int n_qt
   const int q0 = (int)(w % n_qtiles) * kRows;
   const int qi = q0 + tid;
   const float* Q = reinterpret_cast<const float*>(a.q) + bh * (int64_t)a.Nq * D;
-  const float* K = reinterpret_cast<const float*>(a.k) + bh * (int64_t)a.Nk * D;
-  const float* V = reinterpret_cast<const float*>(a.v) + bh * (int64_t)a.Nk * D;
+  const int64_t kvbh = bh / a.kv_group;   // the key/value head this query head reads
+  const float* K = reinterpret_cast<const float*>(a.k) + kvbh * (int64_t)a.Nk * D;
+  const float* V = reinterpret_cast<const float*>(a.v) + kvbh * (int64_t)a.Nk * D;
 
   float q[D], acc[D];
 #pragma unroll
@@ -37,9 +38,11 @@ __global__ __launch_bounds__(kRows) void attn_fwd_f32_kernel(FwdArgs a, int n_qt
   const int qlast = min(q0 + kRows, a.Nq) - 1;
   const int kend = a.causal ? min(a.Nk, qlast + a.diag + 1) : a.Nk;
   const int lim = a.causal ? min(qi + a.diag, a.Nk - 1) : a.Nk - 1;   // last visible key of this row
+  const int low = a.causal ? qi + a.lo : 0;                            // first key of its sliding window
+  const int first_key = a.causal ? q0 + a.lo : 0;                      // ... of the block's first row
   float m_run = -INFINITY, l_run = 0.0f;
 
-  for (int j0 = 0; j0 < kend; j0 += kTk) {
+  for (int j0 = first_key > 0 ? first_key / kTk * kTk : 0; j0 < kend; j0 += kTk) {
     __syncthreads();
     for (int e = tid * 4; e < kTk * D; e += kRows * 4) {
       const int j = j0 + e / D;
@@ -59,7 +62,7 @@ __global__ __launch_bounds__(kRows) void attn_fwd_f32_kernel(FwdArgs a, int n_qt
       float dot = 0.0f;
 #pragma unroll
       for (int c = 0; c < D; ++c) dot = __builtin_fmaf(q[c], Ks[j * D + c], dot);
-      s[j] = (j0 + j <= lim) ? dot : -INFINITY;
+      s[j] = (j0 + j <= lim && j0 + j >= low) ? dot : -INFINITY;
       mx = fmaxf(mx, s[j]);
     }
     const float m_new = fmaxf(m_run, mx * a.scale_log2);

@@ -237,15 +237,15 @@ __device__ __forceinline__ bf16x8 pack_weights(const float (&w)[32], int kk) {
   return __builtin_convertvector(v, bf16x8);
 }
 
-// Hides the keys of a tile that straddles the causal diagonal, in the score accumulators themselves (masking the
-// unpacked copy instead makes the allocator keep both): keys past `lim` (relative to this lane's first key of the
-// tile) are hidden.
-__device__ __forceinline__ void mask_scores(f32x16& s0, f32x16& s1, int lim) {
+// Hides the keys of a tile that straddles the causal diagonal or the lower edge of a sliding window, in the score
+// accumulators themselves (masking the unpacked copy instead makes the allocator keep both): keys past `lim` or
+// before `lo` (both relative to this lane's first key of the tile) are hidden.
+__device__ __forceinline__ void mask_scores(f32x16& s0, f32x16& s1, int lim, int lo) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int kr = 16 * (r >> 3) + (r & 7);
-    if (kr > lim) s0[r] = -INFINITY;
-    if (kr + 32 > lim) s1[r] = -INFINITY;
+    if (kr > lim || kr < lo) s0[r] = -INFINITY;
+    if (kr + 32 > lim || kr + 32 < lo) s1[r] = -INFINITY;
   }
 }
 
@@ -540,8 +540,9 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
   int qt;
   decode_block(n_qtiles, xcd_remap, bh, qt);
   const int q0 = qt * kRows;
-  const __bf16* K = reinterpret_cast<const __bf16*>(a.k) + bh * (int64_t)a.Nk * D;
-  const __bf16* V = reinterpret_cast<const __bf16*>(a.v) + bh * (int64_t)a.Nk * D;
+  const int64_t kvbh = bh / a.kv_group;   // the key/value head this query head reads
+  const __bf16* K = reinterpret_cast<const __bf16*>(a.k) + kvbh * (int64_t)a.Nk * D;
+  const __bf16* V = reinterpret_cast<const __bf16*>(a.v) + kvbh * (int64_t)a.Nk * D;
 
   const int qlast = min(q0 + kRows, a.Nq) - 1;
   const int kend = a.causal ? min(a.Nk, qlast + a.diag + 1) : a.Nk;
@@ -553,18 +554,25 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
 
   // tiles this wave has any visible key in (rows past Nq may see further; they are never stored)
   const int nt_w = min(ntiles, wkend > 0 ? (wkend + kBN - 1) / kBN : 0);
+  // Sliding window: tiles before the first key the block's first row sees are skipped; tiles before `nlow`
+  // hold keys below the window of some row of this wave and are masked.
+  const int first_key = a.causal ? q0 + a.lo : 0;
+  const int t0 = first_key > 0 ? first_key / kBN : 0;
+  const int low_edge = a.causal ? wrow0 + 31 + a.lo : 0;
+  const int nlow = low_edge > 0 ? (low_edge + kBN - 1) / kBN : 0;
   constexpr bool kPipe = pipelined<D>();
 
-  if (ntiles > 0) {
-    issue_copy<D, true, kWaves>(K, 0, a.Nk, k0, wave, lane);
-    issue_copy<D, false, kWaves>(V, 0, a.Nk, v0, wave, lane);
-    if (kPipe && ntiles > 1) issue_copy<D, true, kWaves>(K, kBN, a.Nk, k1, wave, lane);
+  if (ntiles > t0) {
+    issue_copy<D, true, kWaves>(K, t0 * kBN, a.Nk, k0, wave, lane);
+    issue_copy<D, false, kWaves>(V, t0 * kBN, a.Nk, v0, wave, lane);
+    if (kPipe && ntiles > t0 + 1) issue_copy<D, true, kWaves>(K, (t0 + 1) * kBN, a.Nk, k1, wave, lane);
   }
   bf16x8 qf[G::KSTEPS];
   load_q<D>(reinterpret_cast<const __bf16*>(a.q) + (bh * (int64_t)a.Nq + q0) * D, min(kRows, a.Nq - q0),
             wave * 32, lane, qf);
   const LaneAddr<D> la(lane);
   const int row_lim = (a.causal ? min(wrow0 + (lane & 31) + a.diag, a.Nk - 1) : a.Nk - 1) - 8 * la.hi;
+  const int row_lo = (a.causal ? wrow0 + (lane & 31) + a.lo : kNoWindow) - 8 * la.hi;
 
   f32x16 acc[G::CT];
 #pragma unroll
@@ -578,7 +586,7 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
     bf16x8 pb[4];
     float alpha;
     bool need;
-    if (partial) mask_scores(c0, c1, row_lim - t * kBN);
+    if (partial) mask_scores(c0, c1, row_lim - t * kBN, row_lo - t * kBN);
     unpack_scores(c0, c1, w);
     weights_tile(w, pb, m_ref, alpha, need, a.scale_log2);
     rescale_acc<D>(acc, alpha, need);
@@ -595,7 +603,7 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
     f32x16 sa0, sa1, sb0, sb1;
     wait_vmem_all();
     __syncthreads();
-    if (nt_w > 0) qk_tile<D, true>(k0, qf, sa0, sa1, la);
+    if (nt_w > t0) qk_tile<D, true>(k0, qf, sa0, sa1, la);
     auto stage = [&](int t, f32x16& c0, f32x16& c1, f32x16& n0, f32x16& n1, const char* kn, char* kw,
                      const char* vc, char* vw) {
       wait_vmem_all();      // this wave's copies of K tile t+1 and V tile t have landed
@@ -617,7 +625,7 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
       bf16x8 pb[4];
       float alpha, m_use;
       bool need;
-      if (t >= nfull) mask_scores(c0, c1, row_lim - t * kBN);
+      if (t >= nfull || t < nlow) mask_scores(c0, c1, row_lim - t * kBN, row_lo - t * kBN);
       unpack_scores(c0, c1, w);
       // The wave's last tile computes the scores of one more tile, which are never used (K slot `kn` then holds
       // an older tile): one branch-free stage shape keeps the register allocation of the loop tight.
@@ -631,7 +639,7 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
       __builtin_amdgcn_sched_barrier(0);
       stage_phase2<D>(vc, acc, la, w, pb, alpha, m_use, a.scale_log2, l_run, lq_run);
     };
-    for (int t = 0; t < ntiles; t += 2) {
+    for (int t = t0; t < ntiles; t += 2) {
       stage(t, sa0, sa1, sb0, sb1, k1, k0, v0, v1);
       if (t + 1 < ntiles) stage(t + 1, sb0, sb1, sa0, sa1, k0, k1, v1, v0);
     }
@@ -647,9 +655,9 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
       if (t >= nt_w) return;
       f32x16 s0, s1;
       qk_tile<D>(kc, qf, s0, s1, la);
-      plain_tile(s0, s1, t >= nfull, t, vc);
+      plain_tile(s0, s1, t >= nfull || t < nlow, t, vc);
     };
-    for (int t = 0; t < ntiles; t += 2) {
+    for (int t = t0; t < ntiles; t += 2) {
       step(t, k0, v0, k1, v1);
       if (t + 1 < ntiles) step(t + 1, k1, v1, k0, v0);
     }

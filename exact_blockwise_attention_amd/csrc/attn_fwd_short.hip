@@ -40,13 +40,17 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_short_kernel(FwdArgs a, int
 #pragma unroll
   for (int c = 0; c < D / 8; ++c) qv[c] = reinterpret_cast<const bf16x8*>(qrow)[c];
 
-  // Stage K and V of this workgroup's slices (contiguous) in LDS.
-  const int chunks = nseq * a.Nk * (D / 8);
-  const u32x4* Kg = reinterpret_cast<const u32x4*>(reinterpret_cast<const __bf16*>(a.k) + bh0 * a.Nk * D);
-  const u32x4* Vg = reinterpret_cast<const u32x4*>(reinterpret_cast<const __bf16*>(a.v) + bh0 * a.Nk * D);
+  // Stage K and V of this workgroup's slices in LDS (query slice bh reads key/value slice bh / kv_group; with
+  // one key/value head per query head the slices are contiguous).
+  const int per_slice = a.Nk * (D / 8);
+  const int chunks = nseq * per_slice;
+  const u32x4* Kg = reinterpret_cast<const u32x4*>(a.k);
+  const u32x4* Vg = reinterpret_cast<const u32x4*>(a.v);
   for (int e = tid; e < chunks; e += kThreads) {
-    reinterpret_cast<u32x4*>(Kl)[e] = __builtin_nontemporal_load(Kg + e);
-    reinterpret_cast<u32x4*>(Vl)[e] = __builtin_nontemporal_load(Vg + e);
+    const int se = e / per_slice;
+    const int64_t src = ((bh0 + se) / a.kv_group) * (int64_t)per_slice + (e - se * per_slice);
+    reinterpret_cast<u32x4*>(Kl)[e] = __builtin_nontemporal_load(Kg + src);
+    reinterpret_cast<u32x4*>(Vl)[e] = __builtin_nontemporal_load(Vg + src);
   }
   __syncthreads();
   if (!live) return;
@@ -55,6 +59,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_short_kernel(FwdArgs a, int
   const __bf16* Ks = Kl + (int64_t)s * a.Nk * D;
   const __bf16* Vs = Vl + (int64_t)s * a.Nk * D;
   const int lim = a.causal ? min(i + a.diag, a.Nk - 1) : a.Nk - 1;   // last visible key of this row
+  const int low = a.causal ? i + a.lo : 0;                            // first key of its sliding window
 
   // Scores with packed bf16 dot products (v_dot2_f32_bf16: two exact bf16 products added in fp32), two
   // accumulators per key for a shorter dependency chain.
@@ -63,7 +68,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_short_kernel(FwdArgs a, int
 #pragma unroll
   for (int j = 0; j < kShortMax; ++j) {
     sc[j] = -INFINITY;
-    if (j <= lim) {
+    if (j <= lim && j >= low) {
       float d0 = 0.0f, d1 = 0.0f;
 #pragma unroll
       for (int c = 0; c < D / 8; ++c) {
@@ -88,7 +93,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_short_kernel(FwdArgs a, int
   if (mx != -INFINITY) {
 #pragma unroll
     for (int j = 0; j < kShortMax; ++j) {
-      if (j <= lim) {
+      if (j <= lim && j >= low) {
         const float p = __builtin_amdgcn_exp2f(sc[j] - mx);
         l += p;
 #pragma unroll

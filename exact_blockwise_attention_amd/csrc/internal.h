@@ -8,9 +8,14 @@
 namespace ebattn {
 
 // Arguments of one attention-forward launch over B*H independent (batch, head) slices.
-// Layout: q [BH, Nq, d], k/v [BH, Nk, d], o [BH, Nq, d], lse [BH, Nq], all contiguous, d fastest.
-// Causal masking by global position reduces to "key j visible to query i iff j <= i + diag" (host computes
-// diag = floor((q_off - k_off) / pos_stride), clamped); non-causal launches ignore diag.
+// Layout: q [BH, Nq, d], k/v [BH / kv_group, Nk, d], o [BH, Nq, d], lse [BH, Nq], all contiguous, d fastest;
+// query slice bh reads key/value slice bh / kv_group (grouped-query heads: consecutive query heads share one
+// key/value head; kv_group = 1 is plain multi-head attention).
+// Causal masking by global position, with an optional sliding window, reduces to "key j visible to query i iff
+// i + lo <= j <= i + diag" (host computes diag = floor((q_off - k_off) / pos_stride) and, for a window of w
+// positions, lo = floor((q_off - k_off - w) / pos_stride) + 1, both clamped; without a window lo = kNoWindow).
+// Non-causal launches ignore diag and lo.
+constexpr int kNoWindow = -(1 << 30);
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -23,6 +28,8 @@ struct FwdArgs {
   float scale_log2;   // softmax scale times log2(e): the kernels work in the exp2 domain
   int causal;
   int diag;
+  int lo;
+  int kv_group;
 };
 
 // bf16 operands on MFMA; d in {24, 64, 128}; o is bf16 (o_f32 = 0) or fp32 (o_f32 = 1).

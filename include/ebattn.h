@@ -77,6 +77,20 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int H, int Nq, int Nk, int d, float scale, int causal,
              int64_t q_off, int64_t k_off, int pos_stride, int in_dtype, int o_dtype, void* stream);
 
+/* attn_fwd_ex -- attn_fwd with two mask/indexing variants of "架构层解决方案 - Sparse Attention与Ring Attention":
+ *   Hkv         key/value heads (section "MQA与GQA"): k and v are [B,Hkv,Nk,d], Hkv divides H, and query head h
+ *               reads key/value head h / (H/Hkv), so consecutive query heads share one (Hkv = H: attn_fwd;
+ *               Hkv = 1: multi-query attention).
+ *   window      sliding window in positions (section "Sliding Window Attention": each token attends only to the
+ *               w most recent tokens): 0 = none; w > 0 keeps key j for query i iff
+ *               q_pos - w < k_pos <= q_pos (the query's own position included) and requires causal = 1.
+ *   Everything else, errors included, as attn_fwd; attn_fwd(...) equals attn_fwd_ex(..., Hkv = H, window = 0).
+ *   Additional errors: ATTN_EINVAL if Hkv does not divide H, window < 0, or window > 0 without causal. */
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                int64_t q_off, int64_t k_off, int pos_stride, int64_t window, int in_dtype, int o_dtype,
+                void* stream);
+
 /* attn_lse_merge -- merges two partial results over disjoint key sets of the same query rows:
  *   lse = log(exp(lse_a) + exp(lse_b)),  o = exp(lse_a - lse) * o_a + exp(lse_b - lse) * o_b.
  *   Operands are `rows` rows of d values (any [.., rows, d] contiguous layout; for attention rows = B*H*Nq).

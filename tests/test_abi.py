@@ -176,3 +176,39 @@ def test_ring_plan_named_workloads():
         live, kinds = eb.ring_local_plan(16384, [(16384, s) for s in range(4)], causal=True, q_off=r, pos_stride=4)
         assert (live, kinds) == (4, [2, 2, 2, 2])
     assert eb.ring_local_plan(256, [(64, 64 * i) for i in range(4)], causal=False) == (4, [1, 1, 1, 1])
+
+
+def fwd_ex(**kw):
+    args = dict(q=A, k=A + B16, v=A + 2 * B16, o=A + 3 * B16, lse=A + 4 * B16, B=1, H=8, Hkv=2, Nq=64, Nk=64,
+                d=128, scale=0.125, causal=1, q_off=0, k_off=0, stride=1, window=16, it=eb.ATTN_BF16,
+                ot=eb.ATTN_BF16, stream=None)
+    args.update(kw)
+    return lib.attn_fwd_ex(args["q"], args["k"], args["v"], args["o"], args["lse"], args["B"], args["H"],
+                           args["Hkv"], args["Nq"], args["Nk"], args["d"], args["scale"], args["causal"],
+                           args["q_off"], args["k_off"], args["stride"], args["window"], args["it"], args["ot"],
+                           args["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Hkv=3), eb.ATTN_EINVAL),                   # 3 does not divide 8
+    (dict(Hkv=0), eb.ATTN_EINVAL),
+    (dict(Hkv=16), eb.ATTN_EINVAL),
+    (dict(window=-1), eb.ATTN_EINVAL),
+    (dict(window=4, causal=0), eb.ATTN_EINVAL),       # a window needs the causal mask
+    (dict(window=(1 << 62) + 1), eb.ATTN_EINVAL),
+    (dict(q=None), eb.ATTN_EINVAL),
+    (dict(d=32), eb.ATTN_EUNSUPPORTED),
+    (dict(o=A + B16 + 16384), eb.ATTN_EINVAL),        # k holds Hkv = 2 heads (32 KiB): o 16 KiB into it overlaps
+])
+def test_attn_fwd_ex_validation(kw, code):
+    assert fwd_ex(**kw) == code
+    assert eb.last_error() != ""
+
+
+def test_attn_fwd_ex_zero_sized_and_kv_sizing():
+    assert fwd_ex(B=0) == eb.ATTN_OK
+    assert fwd_ex(Nq=0) == eb.ATTN_OK
+    assert fwd_ex(H=0, Hkv=0) == eb.ATTN_OK
+    assert fwd_ex(q=None, B=0) == eb.ATTN_OK
+    # the outputs are sized by the 8 query heads (o: 8 * 64 * 128 bf16 = 128 KiB): lse 64 KiB into o overlaps
+    assert fwd_ex(lse=A + 3 * B16 + 65536) == eb.ATTN_EINVAL

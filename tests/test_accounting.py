@@ -63,3 +63,18 @@ def test_merge_and_fwd_bytes():
     assert acc.merge_bytes(32 * 32768, 128, 4, 4) == 1548 * 1048576
     assert acc.attn_fwd_bytes(1, 1, 10, 10, 4, 2, 2) == 10 * 4 * 2 * 3 + 10 * 4 * 2 + 40
     assert np.isclose(acc.merge_bytes(32 * 32768, 128, 4, 4) / 1e9, 1.623, atol=1e-3)
+
+
+@pytest.mark.parametrize("nq,nk,q_off,k_off,stride,window", [
+    (20, 20, 0, 0, 1, 5), (16, 30, 3, 0, 1, 7), (9, 9, 2, 1, 4, 9), (12, 12, 1, 3, 4, 2), (50, 40, -7, 3, 2, 11),
+    (10, 10, 0, 0, 1, 100), (33, 33, 0, 0, 1, 1)])
+def test_windowed_pair_counts_brute_force(nq, nk, q_off, k_off, stride, window):
+    brute = sum(1 for i in range(nq) for j in range(nk)
+                if q_off + i * stride - window < k_off + j * stride <= q_off + i * stride)
+    assert acc.visible_pairs(nq, nk, True, q_off, k_off, stride, window=window) == brute
+
+
+def test_windowed_pair_count_closed_form():
+    # self-attention over N tokens with a window of w <= N: w(w+1)/2 pairs for the first w rows, w per row after
+    n, w = 32768, 4096
+    assert acc.visible_pairs(n, n, True, window=w) == w * (w + 1) // 2 + (n - w) * w

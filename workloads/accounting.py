@@ -14,13 +14,19 @@ def diag_offset(q_off: int, k_off: int, stride: int) -> int:
     return (int(q_off) - int(k_off)) // int(stride)
 
 
-def visible_pairs(Nq: int, Nk: int, causal: bool, q_off: int = 0, k_off: int = 0, stride: int = 1) -> int:
-    """Number of visible (query, key) pairs of one (batch, head)."""
+def visible_pairs(Nq: int, Nk: int, causal: bool, q_off: int = 0, k_off: int = 0, stride: int = 1,
+                  window: int = 0) -> int:
+    """Number of visible (query, key) pairs of one (batch, head); window > 0 (causal only) keeps the keys of the
+    `window` most recent positions up to each query's own."""
     if not causal:
         return int(Nq) * int(Nk)
     D = diag_offset(q_off, k_off, stride)
     i = np.arange(Nq, dtype=np.int64)
-    return int(np.clip(i + D + 1, 0, Nk).sum())
+    hi = np.clip(i + D + 1, 0, Nk)                      # one past the last visible key
+    if not window:
+        return int(hi.sum())
+    lo = np.clip(i + diag_offset(q_off, k_off + window, stride) + 1, 0, Nk)   # first key inside the window
+    return int(np.maximum(hi - lo, 0).sum())
 
 
 def config_pairs(cfg) -> int:
