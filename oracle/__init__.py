@@ -6,6 +6,7 @@ imports nothing from it; the HIP path never imports it.
 """
 from .attention import (  # noqa: F401
     attention,
+    attention_backward,
     lse_merge,
     lse_merge_many,
     lse_pair,

@@ -18,6 +18,8 @@ Sources (page title, then the section on it):
   [G] "架构层解决方案 - Sparse Attention与Ring Attention", sections "Sliding Window Attention" (each token attends
       only to the w most recent tokens) and "MQA与GQA" (query heads split into g groups, each group sharing one
       key/value head; g = number of heads is plain multi-head attention, g = 1 is MQA).
+  [H] "深度学习注意力机制优化与FlashAttention实践", §4.1 item 3 and §3.3 -- the backward pass recomputes the
+      attention weights instead of storing them (blockwise softmax recomputation).
 
 Readings where the pages are silent or garbled (each also listed in the design notes):
   * lse is the natural log of the sum of exp(scale * q.k) over the visible keys; no additive bias.
@@ -34,6 +36,11 @@ Readings where the pages are silent or garbled (each also listed in the design n
     mask. w = 0 means no window.
   * Grouped-query attention ([G]): with Hkv key/value heads (Hkv divides H) query head h reads key/value head
     h // (H // Hkv), so consecutive query heads share a key/value head, as in the section's figure.
+  * Backward ([H]): the pages name recomputation but give no formulas. The backward here is the exact gradient of
+    the forward definition [A] for a scalar loss whose gradient with respect to o is do, obtained by the chain
+    rule: o = p v, p = softmax of the scaled scores over the visible keys, s = scale q k^T. A key/value head shared
+    by a group of query heads receives the sum of the group's gradients. Rows with no visible key have o = 0
+    independent of every input, so they contribute nothing.
 
 The attention here is the definition, not a blockwise algorithm: each query row's scores over ALL keys are
 materialised at once (rows are processed in chunks only to bound memory), so this code shares no structure with
@@ -159,3 +166,51 @@ def lse_pair(a, b):
         diff = np.abs(a - b)                    # +inf when exactly one side is -inf: the term below is 0
         out = m + np.log1p(np.exp(-diff))
     return np.where(both_empty, -np.inf, out)
+
+
+def attention_backward(q, k, v, do, scale: float, causal: bool = False, q_off: int = 0, k_off: int = 0,
+                       stride: int = 1, window: int = 0):
+    """Gradients of attention ([A], with the masks of [D], [E], [G]) for an output gradient do, in float64 ([H]).
+
+    q: [B, H, Nq, d]; k: [B, Hkv, Nk, d]; v: [B, Hkv, Nk, dv]; do: [B, H, Nq, dv].
+    Returns (dq [B, H, Nq, d], dk [B, Hkv, Nk, d], dv [B, Hkv, Nk, dv], delta [B, H, Nq]).
+
+    The chain rule, one query row i at a time (all of its keys at once, as in the forward definition):
+      p_i = softmax(s_i) over the visible keys (recomputed from q, k: nothing of the forward is stored),
+      dp_ij = do_i . v_j                     (o_i = sum_j p_ij v_j),
+      ds_i = J_i^T dp_i with the softmax Jacobian J_i = diag(p_i) - p_i p_i^T, i.e.
+      ds_ij = p_ij (dp_ij - delta_i), delta_i = sum_j p_ij dp_ij,
+      dq_i = scale sum_j ds_ij k_j,  dk_j += scale ds_ij q_i,  dv_j += p_ij do_i.
+    delta is returned as well: it is the per-row quantity a blockwise backward needs besides the saved lse.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if (k.shape[0] != B or Hkv < 1 or H % Hkv != 0 or v.shape[:3] != (B, Hkv, Nk) or k.shape[3] != d
+            or do.shape != (B, H, Nq, v.shape[3])):
+        raise ValueError("shape mismatch")
+    group = H // Hkv
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    delta = np.zeros((B, H, Nq), dtype=np.float64)
+    chunk = max(1, _CHUNK_ELEMS // max(1, Nk))
+    for c0 in range(0, Nq, chunk):
+        rr = np.arange(c0, min(Nq, c0 + chunk), dtype=np.int64)
+        vis = visible(Nq, Nk, causal, q_off, k_off, stride, rows=rr, window=window)
+        for b in range(B):
+            for h in range(H):
+                g = h // group
+                s = scale * (q[b, h, rr] @ k[b, g].T)            # [r, Nk]
+                p, _ = _softmax_rows(s, vis)                     # recomputed weights ([H]); 0 where masked
+                dp = do[b, h, rr] @ v[b, g].T                    # dL/dp
+                dl = np.sum(p * dp, axis=1)                      # p_i . dp_i (the rank-one part of J_i)
+                ds = p * (dp - dl[:, None])                      # J_i^T dp_i, zero where masked
+                dq[b, h, rr] = scale * (ds @ k[b, g])
+                dk[b, g] += scale * (ds.T @ q[b, h, rr])
+                dv[b, g] += p.T @ do[b, h, rr]
+                delta[b, h, rr] = dl
+    return dq, dk, dv, delta

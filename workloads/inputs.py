@@ -16,7 +16,7 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 # Stable small integers naming the tensors that a workload draws; part of every slab's seed.
-TENSOR_IDS = {"q": 1, "k": 2, "v": 3, "o_a": 4, "o_b": 5, "lse_a": 6, "lse_b": 7}
+TENSOR_IDS = {"q": 1, "k": 2, "v": 3, "o_a": 4, "o_b": 5, "lse_a": 6, "lse_b": 7, "do": 8}
 
 _THREADS = max(1, min(16, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else 8))
 
