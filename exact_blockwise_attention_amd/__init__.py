@@ -9,6 +9,7 @@ Names and semantics follow the C ABI in include/ebattn.h:
 
     o, lse = attn_fwd(q, k, v, scale=..., causal=..., q_off=..., k_off=..., pos_stride=...)
     o, lse = attn_lse_merge(o_a, lse_a, o_b, lse_b)
+    dq, dk, dv, delta = attn_bwd(q, k, v, o, lse, dout, scale=..., causal=..., window=...)
     o, lse = ring_local(q_shard, [(k0, v0, k_off0), (k1, v1, k_off1), ...], scale=..., causal=..., q_off=...)
 """
 from __future__ import annotations
@@ -56,7 +57,7 @@ def _load() -> ctypes.CDLL:
     except ImportError:
         pass
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m exact_blockwise_attention_amd.build` "
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python exact_blockwise_attention_amd/build.py` "
                           "(there is no fallback implementation)")
     lib = ctypes.CDLL(LIB_PATH)
     P, I, I64, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
@@ -64,6 +65,8 @@ def _load() -> ctypes.CDLL:
     lib.attn_fwd.restype = I
     lib.attn_fwd_ex.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, I, I64, I64, I, I64, I, I, P]
     lib.attn_fwd_ex.restype = I
+    lib.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, I64, I64, I, I64, I, I, I, I, P]
+    lib.attn_bwd.restype = I
     lib.attn_lse_merge.argtypes = [P, P, P, P, P, P, I64, I, I, I, P]
     lib.attn_lse_merge.restype = I
     lib.ring_local.argtypes = [P, ctypes.POINTER(KVBlock), I, P, P, I, I, I, I, F, I, I64, I, I, I, P, SZ, P]
@@ -194,6 +197,52 @@ def attn_fwd_ex(q, k, v, *, scale: Optional[float] = None, causal: bool = False,
                            int(causal), int(q_off), int(k_off), int(pos_stride), int(window), _code(q.dtype),
                            _code(out.dtype), _stream(q)))
     return out, lse
+
+
+def attn_bwd(q, k, v, o, lse, dout, *, scale: Optional[float] = None, causal: bool = False, q_off: int = 0,
+             k_off: int = 0, pos_stride: int = 1, window: int = 0, grad_dtype=None, accumulate: bool = False,
+             dq=None, dk=None, dv=None, delta=None) -> Tuple[object, object, object, object]:
+    """Gradients of attn_fwd_ex: q, dout [B,H,Nq,d] bf16, k, v [B,Hkv,Nk,d] bf16, o [B,H,Nq,d] (bf16 or fp32) and
+    lse [B,H,Nq] from the forward over the full key set. Returns (dq, dk, dv, delta) with dq [B,H,Nq,d],
+    dk, dv [B,Hkv,Nk,d] in grad_dtype (default fp32, or the dtype of the given dq) and delta = rowsum(dout * o)
+    [B,H,Nq] fp32. accumulate=True adds into the given fp32 dq, dk, dv."""
+    torch = _torch()
+    _need_cuda(q, k, v, o, lse, dout, dq, dk, dv, delta)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Hkv, Nk, d) or tuple(v.shape) != (B, Hkv, Nk, d):
+        raise ValueError("k and v must be [B, Hkv, Nk, d] with q's B and d")
+    if tuple(o.shape) != (B, H, Nq, d) or tuple(dout.shape) != (B, H, Nq, d) or tuple(lse.shape) != (B, H, Nq):
+        raise ValueError("o and dout must be [B,H,Nq,d] and lse [B,H,Nq]")
+    if k.dtype != q.dtype or v.dtype != q.dtype or dout.dtype != q.dtype:
+        raise TypeError("q, k, v and dout must share a dtype")
+    if lse.dtype != torch.float32:
+        raise TypeError("lse must be float32")
+    if grad_dtype is None:
+        grad_dtype = dq.dtype if dq is not None else torch.float32
+    if accumulate and any(t is None for t in (dq, dk, dv)):
+        raise ValueError("accumulate=True needs dq, dk and dv")
+    if dq is None:
+        dq = torch.empty((B, H, Nq, d), dtype=grad_dtype, device=q.device)
+    if dk is None:
+        dk = torch.empty((B, Hkv, Nk, d), dtype=grad_dtype, device=q.device)
+    if dv is None:
+        dv = torch.empty((B, Hkv, Nk, d), dtype=grad_dtype, device=q.device)
+    if delta is None:
+        delta = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if (tuple(dq.shape) != (B, H, Nq, d) or tuple(dk.shape) != (B, Hkv, Nk, d) or tuple(dv.shape) != (B, Hkv, Nk, d)
+            or tuple(delta.shape) != (B, H, Nq)):
+        raise ValueError("dq must be [B,H,Nq,d], dk and dv [B,Hkv,Nk,d], delta [B,H,Nq]")
+    if dq.dtype != grad_dtype or dk.dtype != grad_dtype or dv.dtype != grad_dtype or delta.dtype != torch.float32:
+        raise TypeError("dq, dk, dv must share grad_dtype and delta must be float32")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _check(lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                        _ptr(delta), B, H, Hkv, Nq, Nk, d, scale, int(causal), int(q_off), int(k_off),
+                        int(pos_stride), int(window), _code(q.dtype), _code(o.dtype), _code(grad_dtype),
+                        int(accumulate), _stream(q)))
+    return dq, dk, dv, delta
 
 
 def attn_lse_merge(o_a, lse_a, o_b, lse_b, *, out=None, lse_out=None, out_dtype=None) -> Tuple[object, object]:

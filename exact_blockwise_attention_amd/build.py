@@ -1,6 +1,6 @@
 """Builds libebattn.so (the HIP kernels and the C ABI) in-tree for gfx950 with hipcc.
 
-    python -m exact_blockwise_attention_amd.build [--jobs N] [--verbose]
+    python exact_blockwise_attention_amd/build.py [--jobs N] [--verbose]
 
 Every HIP source is compiled with packed-fp32 instruction selection disabled (-packed-fp32-ops): the kernels'
 fp32 arithmetic is emitted as scalar VALU instructions.
@@ -22,7 +22,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libebattn.so")
 ARCH = os.environ.get("EBATTN_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["api.hip", "attn_fwd_mfma.hip", "attn_fwd_f32.hip", "attn_fwd_short.hip", "lse_merge.hip"]
+SOURCES = ["api.hip", "attn_fwd_mfma.hip", "attn_fwd_f32.hip", "attn_fwd_short.hip", "attn_bwd_mfma.hip",
+           "lse_merge.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

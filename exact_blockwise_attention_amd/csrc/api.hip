@@ -204,6 +204,83 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
                      o_dtype, stream);
 }
 
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
+             void* dk, void* dv, float* delta, int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+             int64_t q_off, int64_t k_off, int pos_stride, int64_t window, int in_dtype, int o_dtype, int grad_dtype,
+             int accumulate, void* stream) {
+  g_err[0] = '\0';
+  if (B < 0 || H < 0 || Hkv < 0 || Nq < 0 || Nk < 0)
+    return fail(ATTN_EINVAL, "negative size (B=%d H=%d Hkv=%d Nq=%d Nk=%d)", B, H, Hkv, Nq, Nk);
+  if (Nq > ATTN_MAX_SEQ || Nk > ATTN_MAX_SEQ) return fail(ATTN_EINVAL, "Nq or Nk exceeds ATTN_MAX_SEQ");
+  if (H > 0 && (Hkv < 1 || Hkv > H || H % Hkv != 0)) return fail(ATTN_EINVAL, "Hkv=%d must divide H=%d", Hkv, H);
+  if (!(causal == 0 || causal == 1)) return fail(ATTN_EINVAL, "causal must be 0 or 1 (got %d)", causal);
+  if (!(accumulate == 0 || accumulate == 1)) return fail(ATTN_EINVAL, "accumulate must be 0 or 1");
+  if (pos_stride < 1) return fail(ATTN_EINVAL, "pos_stride must be >= 1 (got %d)", pos_stride);
+  if (!(scale > 0.0f) || !isfinite(scale)) return fail(ATTN_EINVAL, "scale must be finite and > 0");
+  if (q_off > kOffLimit || q_off < -kOffLimit || k_off > kOffLimit || k_off < -kOffLimit)
+    return fail(ATTN_EINVAL, "q_off or k_off out of range");
+  if (window < 0 || window > kOffLimit) return fail(ATTN_EINVAL, "window out of range (got %lld)", (long long)window);
+  if (window > 0 && !causal) return fail(ATTN_EINVAL, "a sliding window requires causal = 1");
+  if (!dtype_ok(in_dtype) || !dtype_ok(o_dtype) || !dtype_ok(grad_dtype)) return fail(ATTN_EINVAL, "unknown dtype code");
+  if (in_dtype != ATTN_BF16) return fail(ATTN_EUNSUPPORTED, "the backward takes bf16 q, k, v and dout");
+  if (accumulate && grad_dtype != ATTN_F32) return fail(ATTN_EINVAL, "accumulate requires fp32 gradients");
+  if (d != 64 && d != 128) return fail(ATTN_EUNSUPPORTED, "head dim d=%d not supported by the backward (64, 128)", d);
+  const int64_t BH = (int64_t)B * H, BHkv = (int64_t)B * (H > 0 ? Hkv : 0);
+  const int64_t qrows = BH * Nq, krows = BHkv * Nk;
+  if (qrows == 0 && krows == 0) return ATTN_OK;
+  if (qrows > 0) {
+    if (!q || !o || !lse || !dout || !dq || !delta) return fail(ATTN_EINVAL, "null q, o, lse, dout, dq or delta");
+    if (!aligned(q, 16) || !aligned(o, 16) || !aligned(dout, 16) || !aligned(dq, 16))
+      return fail(ATTN_EINVAL, "q, o, dout and dq must be 16-byte aligned");
+    if (!aligned(lse, 4) || !aligned(delta, 4)) return fail(ATTN_EINVAL, "lse and delta must be 4-byte aligned");
+  }
+  if (krows > 0) {
+    if (!k || !v || !dk || !dv) return fail(ATTN_EINVAL, "null k, v, dk or dv");
+    if (!aligned(k, 16) || !aligned(v, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+      return fail(ATTN_EINVAL, "k, v, dk and dv must be 16-byte aligned");
+  }
+  // the four outputs must not overlap each other or any input
+  const int64_t gb = elem_bytes(grad_dtype);
+  const Span outs[4] = {span(dq, qrows * d * gb), span(dk, krows * d * gb), span(dv, krows * d * gb),
+                        span(delta, qrows * 4)};
+  const Span ins[6] = {span(q, qrows * d * 2), span(k, krows * d * 2), span(v, krows * d * 2),
+                       span(o, qrows * d * elem_bytes(o_dtype)), span(lse, qrows * 4), span(dout, qrows * d * 2)};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j])) return fail(ATTN_EINVAL, "dq, dk, dv and delta must not overlap");
+    for (int j = 0; j < 6; ++j)
+      if (overlap(outs[i], ins[j])) return fail(ATTN_EINVAL, "an output (dq, dk, dv, delta) overlaps an input");
+  }
+  const int diag = diag_offset(q_off, k_off, pos_stride);
+  const int lo = window_lo(q_off, k_off, pos_stride, window);
+  const bool masks = causal && ((int64_t)diag < (int64_t)Nk - 1 || (int64_t)Nq - 1 + lo > 0);
+  ebattn::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.delta = delta;
+  a.BH = BH;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.scale = scale;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.causal = masks ? 1 : 0;
+  a.diag = masks ? diag : 0;
+  a.lo = masks ? lo : ebattn::kNoWindow;
+  a.kv_group = H > 0 ? H / Hkv : 1;
+  a.o_f32 = o_dtype == ATTN_F32;
+  a.accumulate = accumulate;
+  (void)hipGetLastError();  // drop a stale error so a failure below is attributed to this call
+  const hipError_t e = ebattn::launch_attn_bwd_bf16(a, d, grad_dtype == ATTN_F32, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : hip_fail(e, "backward launch");
+}
+
 int attn_lse_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b, void* o, float* lse,
                    int64_t rows, int d, int part_dtype, int o_dtype, void* stream) {
   g_err[0] = '\0';

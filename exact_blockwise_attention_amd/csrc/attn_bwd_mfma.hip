@@ -1,0 +1,554 @@
+// Exact attention backward, bf16 operands on gfx950 MFMA, fp32 accumulation.
+//
+// Method: "深度学习注意力机制优化与FlashAttention实践" §4.1 (item 3) and §3.3 -- the backward recomputes the
+// attention weights tile by tile from the saved per-row log-sum-exp instead of storing them. With
+// P_ij = exp(scale q_i.k_j - lse_i) and delta_i = dO_i . O_i (lse and O over the full key set), the gradient of
+// exact attention is
+//   dV_j = sum_i P_ij dO_i,  dS_ij = P_ij (dO_i . V_j - delta_i),  dQ_i = scale sum_j dS_ij K_j,
+//   dK_j = scale sum_i dS_ij Q_i,
+// a sum of independent (query tile, key tile) terms. That is also what lets one share of a ring run the
+// backward block by block with the global lse and delta and add up the blocks' contributions.
+//
+// Two kernels, so that no gradient needs atomics:
+//   * the dq kernel (runs first) owns 128 query rows per workgroup, 32 per wave with Q and dO held in VGPRs,
+//     and walks the key tiles like the forward: S^T = K Q^T and dP^T = V dO^T put one query row in each lane
+//     (its lse and delta are per-lane scalars), dS^T is formed in registers and dQ^T += K^T dS^T. Before the
+//     loop it forms delta from O and dO and writes it out for the second kernel.
+//   * the dk/dv kernel owns 128 keys of one key/value head, 32 per wave with K and V held in VGPRs, and walks
+//     the query tiles of every query head that reads that key/value head: S = Q K^T and dP = dO V^T put one key
+//     in each lane, and dV^T += dO^T P, dK^T += Q^T dS.
+// Operand layout, shared by both kernels: the rows of the operand read from LDS by rows are taken in an order
+// with bits 2 and 3 of the row index swapped, which leaves the 32x32 MFMA results in registers already laid out
+// as the B operand of the next product (whose k index runs over those rows). The LDS tiles (64 rows of bf16)
+// are read both by rows (16 bytes per lane, contraction over the head dim) and transposed
+// (ds_read_b64_tr_b16, contraction over the rows); one XOR swizzle of the 16-byte chunks of a row keeps both
+// patterns free of bank conflicts on the 64 four-byte banks. Tiles are copied HBM -> LDS by the buffer unit
+// (buffer_load ... lds), double-buffered, one barrier per tile.
+#include "internal.h"
+
+namespace ebattn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int kBT = 64;                        // rows per LDS tile (keys in the dq kernel, queries in dk/dv)
+constexpr int kWaves = 4;                      // waves per workgroup, 32 owned rows each
+constexpr int kOwn = 32 * kWaves;              // owned rows per workgroup
+constexpr int32_t kRsrcWord3 = 0x00020000;     // raw buffer, 32-bit data format (gfx9 family)
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int D>
+struct BG {
+  static_assert(D == 64 || D == 128, "head dim 64 or 128");
+  static constexpr int KSTEPS = D / 16;            // MFMA k-steps over the head dim
+  static constexpr int CT = D / 32;                // 32-row tiles of a transposed (d x rows) result
+  static constexpr int RB = D * 2;                 // bytes of one bf16 row
+  static constexpr int CPR = D / 8;                // 16-byte chunks per row
+  static constexpr int TILE = kBT * RB;
+  static constexpr int INSTR = TILE / 1024;        // wave-wide 16-byte-per-lane copies per tile
+  static constexpr int ROWS_PER_INSTR = 1024 / RB;
+  static constexpr int PER_WAVE = INSTR / kWaves;
+  static_assert(INSTR % kWaves == 0, "tile copy must split evenly over the waves");
+};
+
+// Chunk swizzle of LDS row `row` (XOR on the 16-byte chunk index). Row reads: 16 consecutive lanes read one chunk
+// index of 16 rows that cover row & 15 = 0..15 -> the swizzle must be a bijection of those 16 rows onto distinct
+// bank groups. Transposed reads: 32 lanes read 4 consecutive rows (an aligned group) x 4 chunks of an aligned
+// group of 4 -> the 4 rows must land in 4 different 64-byte quarters of the 256-byte bank row.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+}
+// bits 2 and 3 swapped (an involution)
+__device__ __forceinline__ int perm_row(int p) { return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int32_t n = (int32_t)(bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, kRsrcWord3);
+}
+
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// This wave's share of the HBM -> LDS copy of rows [r0, r0 + 64) of X (rows_total rows of D bf16): natural row
+// order, chunks swizzled. Rows past rows_total read as zero (a tile wholly past the end touches no memory).
+template <int D>
+__device__ __forceinline__ void copy_tile(const __bf16* X, int r0, int rows_total, char* dst, int wave, int lane) {
+  using G = BG<D>;
+  const int valid = max(0, min(kBT, rows_total - r0));
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(X + (int64_t)r0 * D, (int64_t)valid * G::RB);
+  const int sub = lane / G::CPR, pos = lane % G::CPR;
+#pragma unroll
+  for (int i = 0; i < G::PER_WAVE; ++i) {
+    const int instr = wave * G::PER_WAVE + i;
+    const int row = instr * G::ROWS_PER_INSTR + sub;
+    const int m = pos ^ swz<D>(row);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(dst + instr * 1024), 16,
+                                             (uint32_t)((row * D + m * 8) * 2), 0, 0, 0);
+  }
+}
+
+// Per-lane LDS addressing, fixed for the whole kernel.
+template <int D>
+struct Lanes {
+  int hi;                       // lane / 32: which 8-wide half of each 16-wide k-step this lane supplies
+  int row_off;                  // byte offset of this lane's row in a 32-row block: row perm_row(l % 32)
+  int row_sw;                   // its chunk swizzle
+  int tr[2][BG<D>::CT];         // transposed reads: rows 8*hi + (l%16)/4 and 4 rows further, per 32-column tile
+  __device__ explicit Lanes(int lane) {
+    using G = BG<D>;
+    hi = lane >> 5;
+    const int pr = perm_row(lane & 31);
+    row_off = pr * G::RB;
+    row_sw = swz<D>(pr);
+    const int g2 = (lane >> 4) & 1, a4 = (lane & 15) >> 2, b4 = lane & 3;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int row = 8 * hi + 4 * half + a4;
+#pragma unroll
+      for (int ct = 0; ct < G::CT; ++ct) {
+        const int m = 4 * ct + 2 * g2 + (b4 >> 1);   // chunk of columns 32*ct + 16*g2 + 4*b4 .. +3
+        tr[half][ct] = row * G::RB + 16 * (m ^ swz<D>(row)) + 8 * (b4 & 1);
+      }
+    }
+  }
+};
+
+// Row operand (A of a product contracting over the head dim) from an LDS tile: rows 32*blk + perm_row(l%32),
+// head-dim columns 16*ks + 8*hi .. +7.
+template <int D>
+__device__ __forceinline__ bf16x8 row_frag(const char* t, const Lanes<D>& la, int blk, int ks) {
+  const char* p = t + blk * 32 * BG<D>::RB + la.row_off + 16 * ((2 * ks + la.hi) ^ la.row_sw);
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// Transposed operand (A of a product contracting over the tile rows): head-dim columns 32*ct + l%32, tile rows
+// 16*kk + 8*hi .. +7 (two transpose reads of 4 rows each).
+template <int D>
+__device__ __forceinline__ bf16x8 tr_frag(const char* t, const Lanes<D>& la, int kk, int ct) {
+  const char* p = t + kk * 16 * BG<D>::RB;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + la.tr[0][ct]));
+  const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + la.tr[1][ct]));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// B-operand fragments of 32 rows held in VGPRs: lane holds row row0 + l%32, head-dim columns 16*ks + 8*hi .. +7;
+// rows past rows_total read as zero.
+template <int D>
+__device__ __forceinline__ void load_frags(const __bf16* X, int row0, int rows_total, int lane,
+                                           bf16x8 (&f)[BG<D>::KSTEPS]) {
+  const int valid = max(0, min(32, rows_total - row0));
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(X + (int64_t)row0 * D, (int64_t)valid * D * 2);
+  const int l32 = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int ks = 0; ks < BG<D>::KSTEPS; ++ks)
+    f[ks] = __builtin_bit_cast(bf16x8,
+                               __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)((l32 * D + 16 * ks + 8 * hi) * 2), 0, 0));
+}
+
+// Writes factor * acc for 32 rows (row0 + l%32) of a gradient [rows_total, D] at `out` (fp32 or bf16): register r
+// of tile ct holds head-dim column 32*ct + 8*(r/4) + 4*hi + r%4. With `accumulate` (fp32 only) the previous
+// contents are added. Rows past rows_total are dropped by the buffer range.
+template <int D, bool GF32>
+__device__ __forceinline__ void store_grad(void* out, int row0, int rows_total, int lane,
+                                           const f32x16 (&acc)[BG<D>::CT], float factor, bool accumulate) {
+  const int valid = max(0, min(32, rows_total - row0));
+  const int hi = lane >> 5, l32 = lane & 31;
+  const __amdgpu_buffer_rsrc_t r =
+      GF32 ? make_rsrc(reinterpret_cast<float*>(out) + (int64_t)row0 * D, (int64_t)valid * D * 4)
+           : make_rsrc(reinterpret_cast<__bf16*>(out) + (int64_t)row0 * D, (int64_t)valid * D * 2);
+#pragma unroll
+  for (int ct = 0; ct < BG<D>::CT; ++ct)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int c = 32 * ct + 8 * g + 4 * hi;
+      f32x4 y = {acc[ct][4 * g] * factor, acc[ct][4 * g + 1] * factor, acc[ct][4 * g + 2] * factor,
+                 acc[ct][4 * g + 3] * factor};
+      if constexpr (GF32) {
+        const uint32_t off = (uint32_t)((l32 * D + c) * 4);
+        if (accumulate) y += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, y), r, off, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, __builtin_convertvector(y, bf16x4)), r,
+                                              (uint32_t)((l32 * D + c) * 2), 0, 0);
+      }
+    }
+}
+
+// lse (natural log) -> the exp2-domain subtrahend of the weights; a row with no visible key (lse = -inf) gets
+// +inf so that all of its weights are exactly zero.
+__device__ __forceinline__ float lse_to_sub(float lse) { return lse == -INFINITY ? INFINITY : lse * kLog2e; }
+
+// Workgroup -> (slice, tile). Workgroups are dispatched round-robin over the 8 XCDs; each XCD gets a contiguous
+// range of slices so that the tiles one slice re-reads stay in one L2.
+__device__ __forceinline__ void decode_block(int n_tiles, int xcd_remap, int64_t& slice, int& tile) {
+  int64_t w = blockIdx.x;
+  if (xcd_remap) w = (w & 7) * ((int64_t)gridDim.x >> 3) + (w >> 3);
+  slice = w / n_tiles;
+  tile = (int)(w % n_tiles);
+}
+
+// ------------------------------------------------------------------------------------------------------------
+// dq kernel (and delta): 128 query rows per workgroup, key tiles of 64.
+
+template <int D, bool GF32>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_dq_kernel(BwdArgs a, int n_qtiles, int xcd_remap) {
+  using G = BG<D>;
+  __shared__ __attribute__((aligned(1024))) char k0[G::TILE];
+  __shared__ __attribute__((aligned(1024))) char k1[G::TILE];
+  __shared__ __attribute__((aligned(1024))) char v0[G::TILE];
+  __shared__ __attribute__((aligned(1024))) char v1[G::TILE];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int64_t bh;
+  int qt;
+  decode_block(n_qtiles, xcd_remap, bh, qt);
+  qt = n_qtiles - 1 - qt;    // the heaviest causal block (the last query rows) first
+  const int q0 = qt * kOwn;
+  const int64_t kvbh = bh / a.kv_group;
+  const __bf16* K = reinterpret_cast<const __bf16*>(a.k) + kvbh * (int64_t)a.Nk * D;
+  const __bf16* V = reinterpret_cast<const __bf16*>(a.v) + kvbh * (int64_t)a.Nk * D;
+  const int64_t qbase = bh * (int64_t)a.Nq;   // first row of this query slice
+
+  // key-tile range of the block and of this wave (as in the forward)
+  const int qlast = min(q0 + kOwn, a.Nq) - 1;
+  const int kend = a.causal ? min(a.Nk, qlast + a.diag + 1) : a.Nk;
+  const int ntiles = kend > 0 ? (kend + kBT - 1) / kBT : 0;
+  const int wrow0 = q0 + wave * 32;
+  const int wkfull = a.causal ? min(a.Nk, wrow0 + a.diag + 1) : a.Nk;
+  const int nfull = wkfull > 0 ? wkfull / kBT : 0;
+  const int wkend = a.causal ? min(a.Nk, wrow0 + 31 + a.diag + 1) : a.Nk;
+  const int nt_w = min(ntiles, wkend > 0 ? (wkend + kBT - 1) / kBT : 0);
+  const int first_key = a.causal ? q0 + a.lo : 0;
+  const int t0 = first_key > 0 ? first_key / kBT : 0;
+  const int low_edge = a.causal ? wrow0 + 31 + a.lo : 0;
+  const int nlow = low_edge > 0 ? (low_edge + kBT - 1) / kBT : 0;
+
+  if (ntiles > t0) {
+    copy_tile<D>(K, t0 * kBT, a.Nk, k0, wave, lane);
+    copy_tile<D>(V, t0 * kBT, a.Nk, v0, wave, lane);
+  }
+
+  // Q and dO of this wave's rows as B operands; delta_i = dO_i . O_i over this lane's half of the head dim plus
+  // its partner lane's half.
+  bf16x8 qf[G::KSTEPS], df[G::KSTEPS];
+  const __bf16* Qs = reinterpret_cast<const __bf16*>(a.q) + qbase * D;
+  const __bf16* dOs = reinterpret_cast<const __bf16*>(a.dout) + qbase * D;
+  load_frags<D>(Qs, wrow0, a.Nq, lane, qf);
+  load_frags<D>(dOs, wrow0, a.Nq, lane, df);
+  const int hi = lane >> 5;
+  const int row = wrow0 + (lane & 31);
+  float dl = 0.0f;
+  {
+    const int valid = max(0, min(32, a.Nq - wrow0));
+    if (a.o_f32) {
+      const __amdgpu_buffer_rsrc_t r = make_rsrc(reinterpret_cast<const float*>(a.o) + (qbase + wrow0) * D,
+                                                 (int64_t)valid * D * 4);
+#pragma unroll
+      for (int ks = 0; ks < G::KSTEPS; ++ks) {
+        const uint32_t off = (uint32_t)((((lane & 31) * D) + 16 * ks + 8 * hi) * 4);
+        const f32x4 x0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+        const f32x4 x1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0));
+        const f32x8 g = __builtin_convertvector(df[ks], f32x8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dl = __builtin_fmaf(g[e], x0[e], __builtin_fmaf(g[4 + e], x1[e], dl));
+      }
+    } else {
+      bf16x8 of[G::KSTEPS];
+      load_frags<D>(reinterpret_cast<const __bf16*>(a.o) + qbase * D, wrow0, a.Nq, lane, of);
+#pragma unroll
+      for (int ks = 0; ks < G::KSTEPS; ++ks) {
+        const f32x8 x = __builtin_convertvector(of[ks], f32x8);
+        const f32x8 g = __builtin_convertvector(df[ks], f32x8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dl = __builtin_fmaf(g[e], x[e], dl);
+      }
+    }
+  }
+  dl = pair_sum(dl);
+  const float lsub = row < a.Nq ? lse_to_sub(a.lse[qbase + row]) : INFINITY;
+  if (hi == 0 && row < a.Nq) a.delta[qbase + row] = dl;
+
+  const Lanes<D> la(lane);
+  const int row_lim = (a.causal ? min(row + a.diag, a.Nk - 1) : a.Nk - 1) - 8 * hi;
+  const int row_lo = (a.causal ? row + a.lo : kNoWindow) - 8 * hi;
+
+  f32x16 acc[G::CT];
+#pragma unroll
+  for (int ct = 0; ct < G::CT; ++ct) acc[ct] = f32x16{};
+
+  auto step = [&](int t, const char* kc, const char* vc, char* kn, char* vn) {
+    wait_vmem_all();      // this wave's copies of tile t have landed
+    __syncthreads();      // every wave's have; every wave is done with tile t-1
+    if (t + 1 < ntiles) {
+      copy_tile<D>(K, (t + 1) * kBT, a.Nk, kn, wave, lane);
+      copy_tile<D>(V, (t + 1) * kBT, a.Nk, vn, wave, lane);
+    }
+    if (t >= nt_w) return;
+    f32x16 s0 = f32x16{}, s1 = f32x16{}, p0 = f32x16{}, p1 = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < G::KSTEPS; ++ks) {
+      s0 = mfma(row_frag<D>(kc, la, 0, ks), qf[ks], s0);
+      s1 = mfma(row_frag<D>(kc, la, 1, ks), qf[ks], s1);
+      p0 = mfma(row_frag<D>(vc, la, 0, ks), df[ks], p0);
+      p1 = mfma(row_frag<D>(vc, la, 1, ks), df[ks], p1);
+    }
+    // register r of s0/s1 holds key 32*h + 16*(r/8) + 8*hi + r%8 of the tile (h = 0/1)
+    if (t >= nfull || t < nlow) {
+      const int lim = row_lim - t * kBT, lo = row_lo - t * kBT;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kr = 16 * (r >> 3) + (r & 7);
+        if (kr > lim || kr < lo) s0[r] = -INFINITY;
+        if (kr + 32 > lim || kr + 32 < lo) s1[r] = -INFINITY;
+      }
+    }
+    bf16x8 db[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      f32x8 x;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 8 * (kk & 1) + e;
+        const float sv = (kk >> 1) ? s1[r] : s0[r];
+        const float pv = (kk >> 1) ? p1[r] : p0[r];
+        const float pw = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, a.scale_log2, -lsub));
+        x[e] = pw * (pv - dl);
+      }
+      db[kk] = __builtin_convertvector(x, bf16x8);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int ct = 0; ct < G::CT; ++ct) acc[ct] = mfma(tr_frag<D>(kc, la, kk, ct), db[kk], acc[ct]);
+  };
+  for (int t = t0; t < ntiles; t += 2) {
+    step(t, k0, v0, k1, v1);
+    if (t + 1 < ntiles) step(t + 1, k1, v1, k0, v0);
+  }
+  store_grad<D, GF32>(reinterpret_cast<char*>(a.dq) + qbase * D * (GF32 ? 4 : 2), wrow0, a.Nq, lane, acc, a.scale,
+                      a.accumulate != 0);
+}
+
+// ------------------------------------------------------------------------------------------------------------
+// dk/dv kernel: 128 keys of one key/value head per workgroup; query tiles of 64 of every query head in its group.
+
+template <int D, bool GF32>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int xcd_remap) {
+  using G = BG<D>;
+  __shared__ __attribute__((aligned(1024))) char qa[G::TILE];
+  __shared__ __attribute__((aligned(1024))) char qb[G::TILE];
+  __shared__ __attribute__((aligned(1024))) char oa[G::TILE];
+  __shared__ __attribute__((aligned(1024))) char ob[G::TILE];
+  __shared__ __attribute__((aligned(16))) float la_[kBT];   // exp2-domain lse of the tile rows, slot a
+  __shared__ __attribute__((aligned(16))) float lb_[kBT];
+  __shared__ __attribute__((aligned(16))) float da_[kBT];   // delta of the tile rows
+  __shared__ __attribute__((aligned(16))) float db_[kBT];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int64_t kvbh;
+  int kt;
+  decode_block(n_ktiles, xcd_remap, kvbh, kt);   // ascending key tiles: under a causal mask the first see most
+  const int k0 = kt * kOwn;
+  const int kw0 = k0 + wave * 32;
+  const int group = a.kv_group;
+  const int64_t bh0 = kvbh * group;             // the first query slice that reads this key/value slice
+
+  // query range of the block: rows i with i + lo <= j <= i + diag for some key j of the block
+  int qbeg = 0, qend = a.Nq;
+  if (a.causal) {
+    qbeg = max(0, k0 - a.diag);
+    if (a.lo != kNoWindow) qend = min(a.Nq, k0 + kOwn - 1 - a.lo + 1);
+  }
+  const int t0 = qbeg / kBT;
+  const int nt = qend > qbeg ? (qend + kBT - 1) / kBT - t0 : 0;
+  const int nstages = nt * group;
+
+  const __bf16* Q = reinterpret_cast<const __bf16*>(a.q);
+  const __bf16* dO = reinterpret_cast<const __bf16*>(a.dout);
+  auto issue_stage = [&](int s, char* qd, char* od) {
+    const int64_t bh = bh0 + s / nt;
+    const int r0 = (t0 + s % nt) * kBT;
+    copy_tile<D>(Q + bh * a.Nq * D, r0, a.Nq, qd, wave, lane);
+    copy_tile<D>(dO + bh * a.Nq * D, r0, a.Nq, od, wave, lane);
+  };
+  // wave 0 stages the per-row lse (as the exp2-domain subtrahend) and delta of a stage's 64 rows
+  auto load_rows = [&](int s, float& lv, float& dv) {
+    const int64_t bh = bh0 + s / nt;
+    const int i = (t0 + s % nt) * kBT + lane;
+    lv = INFINITY;
+    dv = 0.0f;
+    if (i < a.Nq) {
+      lv = lse_to_sub(a.lse[bh * a.Nq + i]);
+      dv = a.delta[bh * a.Nq + i];
+    }
+  };
+
+  if (nstages > 0) {
+    issue_stage(0, qa, oa);
+    if (wave == 0) {
+      float lv, dv;
+      load_rows(0, lv, dv);
+      la_[lane] = lv;
+      da_[lane] = dv;
+    }
+  }
+
+  const __bf16* Ks = reinterpret_cast<const __bf16*>(a.k) + kvbh * (int64_t)a.Nk * D;
+  const __bf16* Vs = reinterpret_cast<const __bf16*>(a.v) + kvbh * (int64_t)a.Nk * D;
+  bf16x8 kf[G::KSTEPS], vf[G::KSTEPS];
+  load_frags<D>(Ks, kw0, a.Nk, lane, kf);
+  load_frags<D>(Vs, kw0, a.Nk, lane, vf);
+  const Lanes<D> la(lane);
+  const int hi = lane >> 5;
+  const int key = kw0 + (lane & 31);
+  // this lane's key is visible to query rows [key - diag, key - lo]; relative to register r's row offset
+  // 16*(r/8) + 8*hi + r%8 within a 32-row block
+  const int vis_lo = (a.causal ? key - a.diag : -(1 << 30)) - 8 * hi;
+  const int vis_hi = (a.causal && a.lo != kNoWindow ? key - a.lo : (1 << 30)) - 8 * hi;
+  // rows for which every key of this wave is visible: [kw0 + 31 - diag, kw0 - lo]; rows seen by some key of the
+  // wave: [kw0 - diag, kw0 + 31 - lo]
+  const int all_lo = a.causal ? kw0 + 31 - a.diag : -(1 << 30);
+  const int all_hi = a.causal && a.lo != kNoWindow ? kw0 - a.lo : (1 << 30);
+  const int any_lo = a.causal ? kw0 - a.diag : -(1 << 30);
+  const int any_hi = a.causal && a.lo != kNoWindow ? kw0 + 31 - a.lo : (1 << 30);
+
+  f32x16 dk[G::CT], dv[G::CT];
+#pragma unroll
+  for (int ct = 0; ct < G::CT; ++ct) {
+    dk[ct] = f32x16{};
+    dv[ct] = f32x16{};
+  }
+
+  auto step = [&](int s, const char* qc, const char* oc, const float* lc, const float* dc, char* qn, char* on,
+                  float* ln, float* dn) {
+    wait_vmem_all();
+    __syncthreads();
+    float lv = 0.0f, dvv = 0.0f;
+    const bool more = s + 1 < nstages;
+    if (more) {
+      issue_stage(s + 1, qn, on);
+      if (wave == 0) load_rows(s + 1, lv, dvv);
+    }
+    const int i0 = (t0 + s % nt) * kBT;
+    if (i0 + kBT - 1 >= any_lo && i0 <= any_hi) {
+      f32x16 s0 = f32x16{}, s1 = f32x16{}, p0 = f32x16{}, p1 = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < G::KSTEPS; ++ks) {
+        s0 = mfma(row_frag<D>(qc, la, 0, ks), kf[ks], s0);
+        s1 = mfma(row_frag<D>(qc, la, 1, ks), kf[ks], s1);
+        p0 = mfma(row_frag<D>(oc, la, 0, ks), vf[ks], p0);
+        p1 = mfma(row_frag<D>(oc, la, 1, ks), vf[ks], p1);
+      }
+      // register r of s0/s1 holds query row 32*h + 16*(r/8) + 8*hi + r%8 of the tile (h = 0/1)
+      if (!(i0 >= all_lo && i0 + kBT - 1 <= all_hi)) {
+        const int lo = vis_lo - i0, up = vis_hi - i0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qr = 16 * (r >> 3) + (r & 7);
+          if (qr < lo || qr > up) s0[r] = -INFINITY;
+          if (qr + 32 < lo || qr + 32 > up) s1[r] = -INFINITY;
+        }
+      }
+      bf16x8 pb[4], sb[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int rb = 16 * kk + 8 * hi;   // tile row of register 8*(kk&1) of block kk>>1
+        const f32x4 l0 = *reinterpret_cast<const f32x4*>(lc + rb);
+        const f32x4 l1 = *reinterpret_cast<const f32x4*>(lc + rb + 4);
+        const f32x4 e0 = *reinterpret_cast<const f32x4*>(dc + rb);
+        const f32x4 e1 = *reinterpret_cast<const f32x4*>(dc + rb + 4);
+        f32x8 x, y;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * (kk & 1) + e;
+          const float sv = (kk >> 1) ? s1[r] : s0[r];
+          const float pv = (kk >> 1) ? p1[r] : p0[r];
+          const float ls = e < 4 ? l0[e] : l1[e - 4];
+          const float de = e < 4 ? e0[e] : e1[e - 4];
+          const float pw = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, a.scale_log2, -ls));
+          x[e] = pw;
+          y[e] = pw * (pv - de);
+        }
+        pb[kk] = __builtin_convertvector(x, bf16x8);
+        sb[kk] = __builtin_convertvector(y, bf16x8);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int ct = 0; ct < G::CT; ++ct) {
+          dv[ct] = mfma(tr_frag<D>(oc, la, kk, ct), pb[kk], dv[ct]);
+          dk[ct] = mfma(tr_frag<D>(qc, la, kk, ct), sb[kk], dk[ct]);
+        }
+    }
+    if (more && wave == 0) {
+      ln[lane] = lv;
+      dn[lane] = dvv;
+    }
+  };
+  for (int s = 0; s < nstages; s += 2) {
+    step(s, qa, oa, la_, da_, qb, ob, lb_, db_);
+    if (s + 1 < nstages) step(s + 1, qb, ob, lb_, db_, qa, oa, la_, da_);
+  }
+  const int64_t kvrow = kvbh * (int64_t)a.Nk;
+  store_grad<D, GF32>(reinterpret_cast<char*>(a.dk) + kvrow * D * (GF32 ? 4 : 2), kw0, a.Nk, lane, dk, a.scale,
+                      a.accumulate != 0);
+  store_grad<D, GF32>(reinterpret_cast<char*>(a.dv) + kvrow * D * (GF32 ? 4 : 2), kw0, a.Nk, lane, dv, 1.0f,
+                      a.accumulate != 0);
+}
+
+template <int D, bool GF32>
+hipError_t launch_d(const BwdArgs& a, hipStream_t stream) {
+  if (a.BH > 0 && a.Nq > 0) {
+    const int n_qtiles = (a.Nq + kOwn - 1) / kOwn;
+    const int64_t total = (int64_t)n_qtiles * a.BH;
+    if (total > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, GF32>), dim3((unsigned)total), dim3(64 * kWaves), 0, stream, a,
+                       n_qtiles, total % 8 == 0 ? 1 : 0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t BHkv = a.BH / a.kv_group;
+  if (BHkv > 0 && a.Nk > 0) {
+    const int n_ktiles = (a.Nk + kOwn - 1) / kOwn;
+    const int64_t total = (int64_t)n_ktiles * BHkv;
+    if (total > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, GF32>), dim3((unsigned)total), dim3(64 * kWaves), 0, stream, a,
+                       n_ktiles, total % 8 == 0 ? 1 : 0);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd_bf16(const BwdArgs& a, int d, int grad_f32, hipStream_t stream) {
+  switch (d) {
+    case 128: return grad_f32 ? launch_d<128, true>(a, stream) : launch_d<128, false>(a, stream);
+    case 64: return grad_f32 ? launch_d<64, true>(a, stream) : launch_d<64, false>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace ebattn

@@ -41,6 +41,36 @@ hipError_t launch_attn_fwd_f32(const FwdArgs& a, int d, hipStream_t stream);
 constexpr int kShortMax = 16;
 hipError_t launch_attn_fwd_short(const FwdArgs& a, int d, int o_f32, hipStream_t stream);
 
+// Arguments of one attention-backward call (both kernels). q, dout, dq: [BH, Nq, d]; k, v, dk, dv:
+// [BH / kv_group, Nk, d]; o: [BH, Nq, d] (bf16, or fp32 when o_f32); lse, delta: [BH, Nq]. lse and o are the
+// forward's results over the full key set; delta receives rowsum(dout * o). Masks as in FwdArgs.
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;
+  int64_t BH;
+  int Nq;
+  int Nk;
+  float scale;        // the softmax scale: the factor of dq and dk
+  float scale_log2;   // scale * log2(e)
+  int causal;
+  int diag;
+  int lo;
+  int kv_group;
+  int o_f32;          // o is fp32 (else bf16)
+  int accumulate;     // add into dq, dk, dv instead of overwriting (fp32 gradients only)
+};
+// bf16 q, k, v, dout on MFMA; d in {64, 128}; gradients fp32 (grad_f32 = 1) or bf16. The dq kernel (which also
+// writes delta) runs first, then the dk/dv kernel, both on `stream`.
+hipError_t launch_attn_bwd_bf16(const BwdArgs& a, int d, int grad_f32, hipStream_t stream);
+
 struct MergeArgs {
   const void* o_a;
   const float* lse_a;

@@ -91,6 +91,35 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
                 int64_t q_off, int64_t k_off, int pos_stride, int64_t window, int in_dtype, int o_dtype,
                 void* stream);
 
+/* attn_bwd -- gradients of exact attention (the backward pass of attn_fwd_ex), with the attention weights
+ * recomputed tile by tile from the saved lse instead of stored ("深度学习注意力机制优化与FlashAttention实践"
+ * §4.1 item 3 and §3.3). For an output gradient dout = dL/do:
+ *   P_ij = exp(scale q_i.k_j - lse_i) on visible pairs (0 elsewhere), delta_i = dout_i . o_i,
+ *   dv_j = sum_i P_ij dout_i,  ds_ij = P_ij (dout_i . v_j - delta_i),
+ *   dq_i = scale sum_j ds_ij k_j,  dk_j = scale sum_i ds_ij q_i,
+ * summed over the query heads of a group for a shared key/value head. These are the exact gradients of the
+ * forward when lse and o are the forward's results over the same keys. When k, v are one block of a larger key
+ * set (a ring share), pass the lse and o of the FULL key set: the returned dq is then that block's contribution
+ * (dq over the full set is the sum over the blocks; see `accumulate`), and dk, dv are exact for the block's keys.
+ *   q, dout      bf16 [B,H,Nq,d]; k, v bf16 [B,Hkv,Nk,d] (Hkv divides H, as attn_fwd_ex).
+ *   o            [B,H,Nq,d] in o_dtype (ATTN_BF16 or ATTN_F32); lse fp32 [B,H,Nq] (-inf rows contribute nothing).
+ *   dq           [B,H,Nq,d], dk, dv [B,Hkv,Nk,d], in grad_dtype (ATTN_F32 or ATTN_BF16); written.
+ *   delta        fp32 [B,H,Nq], written with rowsum(dout * o) (a per-row value the caller may reuse).
+ *   accumulate   0: overwrite dq, dk, dv; 1: add into them (ATTN_F32 gradients only).
+ *   in_dtype     ATTN_BF16 only (ATTN_EUNSUPPORTED otherwise); d in {64, 128} (ATTN_EUNSUPPORTED otherwise).
+ *   Masks, offsets, window, scale, stream: as attn_fwd_ex.
+ *   Sizes        B, H, Hkv, Nq, Nk >= 0; Nq = 0 writes zero dk, dv (or leaves them, with accumulate); Nk = 0 or
+ *                a mask that hides every key writes zero dq; pointers of zero-sized tensors may be NULL.
+ *   Overlap      dq, dk, dv and delta must not overlap each other or any input (ATTN_EINVAL).
+ *   Numerics     bf16 MFMA products with fp32 accumulation: P is rounded to bf16 for dv and ds to bf16 for dq
+ *                and dk; lse, delta and the exponentials are fp32.
+ *   Two kernels run in order on `stream`: dq (which also writes delta), then dk and dv. */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+             void* dq, void* dk, void* dv, float* delta,
+             int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+             int64_t q_off, int64_t k_off, int pos_stride, int64_t window,
+             int in_dtype, int o_dtype, int grad_dtype, int accumulate, void* stream);
+
 /* attn_lse_merge -- merges two partial results over disjoint key sets of the same query rows:
  *   lse = log(exp(lse_a) + exp(lse_b)),  o = exp(lse_a - lse) * o_a + exp(lse_b - lse) * o_b.
  *   Operands are `rows` rows of d values (any [.., rows, d] contiguous layout; for attention rows = B*H*Nq).

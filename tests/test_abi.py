@@ -212,3 +212,52 @@ def test_attn_fwd_ex_zero_sized_and_kv_sizing():
     assert fwd_ex(q=None, B=0) == eb.ATTN_OK
     # the outputs are sized by the 8 query heads (o: 8 * 64 * 128 bf16 = 128 KiB): lse 64 KiB into o overlaps
     assert fwd_ex(lse=A + 3 * B16 + 65536) == eb.ATTN_EINVAL
+
+
+def bwd(**kw):
+    args = dict(q=A, k=A + B16, v=A + 2 * B16, o=A + 3 * B16, lse=A + 4 * B16, do=A + 5 * B16, dq=A + 6 * B16,
+                dk=A + 7 * B16, dv=A + 8 * B16, delta=A + 9 * B16, B=1, H=8, Hkv=2, Nq=64, Nk=64, d=128,
+                scale=0.125, causal=1, q_off=0, k_off=0, stride=1, window=0, it=eb.ATTN_BF16, ot=eb.ATTN_BF16,
+                gt=eb.ATTN_F32, acc=0, stream=None)
+    args.update(kw)
+    return lib.attn_bwd(args["q"], args["k"], args["v"], args["o"], args["lse"], args["do"], args["dq"], args["dk"],
+                        args["dv"], args["delta"], args["B"], args["H"], args["Hkv"], args["Nq"], args["Nk"],
+                        args["d"], args["scale"], args["causal"], args["q_off"], args["k_off"], args["stride"],
+                        args["window"], args["it"], args["ot"], args["gt"], args["acc"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), eb.ATTN_EINVAL),
+    (dict(do=None), eb.ATTN_EINVAL),
+    (dict(delta=None), eb.ATTN_EINVAL),
+    (dict(dk=None), eb.ATTN_EINVAL),
+    (dict(Hkv=3), eb.ATTN_EINVAL),
+    (dict(Nk=-1), eb.ATTN_EINVAL),
+    (dict(causal=2), eb.ATTN_EINVAL),
+    (dict(acc=2), eb.ATTN_EINVAL),
+    (dict(acc=1, gt=eb.ATTN_BF16), eb.ATTN_EINVAL),        # accumulation needs fp32 gradients
+    (dict(window=8, causal=0), eb.ATTN_EINVAL),
+    (dict(scale=0.0), eb.ATTN_EINVAL),
+    (dict(stride=0), eb.ATTN_EINVAL),
+    (dict(it=eb.ATTN_F32), eb.ATTN_EUNSUPPORTED),           # the backward takes bf16 inputs
+    (dict(it=7), eb.ATTN_EINVAL),
+    (dict(d=24), eb.ATTN_EUNSUPPORTED),
+    (dict(dq=A + 1), eb.ATTN_EINVAL),                       # misaligned
+    (dict(delta=A + 2), eb.ATTN_EINVAL),
+    (dict(dq=A + 3 * B16 + 4096), eb.ATTN_EINVAL),          # dq overlaps o
+    (dict(dv=A + 7 * B16 + 4096), eb.ATTN_EINVAL),          # dv overlaps dk (2 heads x 64 x 128 fp32 = 64 KiB)
+    (dict(delta=A + 6 * B16 + 8), eb.ATTN_EINVAL),          # delta inside dq
+    (dict(dk=A + 4 * B16), eb.ATTN_EINVAL),                 # dk over lse
+])
+def test_attn_bwd_validation(kw, code):
+    assert bwd(**kw) == code
+    assert eb.last_error() != ""
+
+
+def test_attn_bwd_zero_sized_calls_are_noops():
+    assert bwd(B=0) == eb.ATTN_OK
+    assert bwd(H=0, Hkv=0) == eb.ATTN_OK
+    assert bwd(Nq=0, Nk=0) == eb.ATTN_OK
+    assert bwd(B=0, q=None, k=None, v=None, o=None, lse=None, do=None, dq=None, dk=None, dv=None, delta=None) == eb.ATTN_OK
+    # with Nq = 0 the query-side pointers are not needed, but dk and dv still are
+    assert bwd(Nq=0, dk=None) == eb.ATTN_EINVAL
