@@ -1,6 +1,6 @@
 """Benchmark of the exact blockwise attention forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu] [--copy-probe BYTES] [--merge-only]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu] [--copy-probe BYTES] [--merge-only] [--bwd-only]
 
 A step is one attention forward (scores, causal mask by position, online softmax, P.V, epilogue) over the
 causal self-attention workload B=4, H=32, N=8192, d=128, bf16 in / bf16 out with fp32 lse, inputs iid N(0,1)
@@ -12,8 +12,8 @@ seeded and already resident in HBM. The printed JSON line reports:
              source, else null;
   cpu_baseline  the float64 oracle timed on this host on a bounded row sample of the same workload;
   extra      secondary measurements: the LSE merge at the ring-share shape (HBM-bound), the ring-share /
-             striped workloads end to end, both axes of the tabular workload, and a sliding-window
-             grouped-query shape (attn_fwd_ex).
+             striped workloads end to end, both axes of the tabular workload, a sliding-window
+             grouped-query shape (attn_fwd_ex), and the backward (attn_bwd) on the forward's workload.
 """
 from __future__ import annotations
 
@@ -179,6 +179,8 @@ def bench_extra(torch, eb, dev, steps):
     out.update(bench_tabular(torch, eb, dev, steps))
     torch.cuda.empty_cache()
     out.update(bench_window_gqa(torch, eb, dev, steps))
+    torch.cuda.empty_cache()
+    out.update(bench_backward(torch, eb, dev, steps))
     return out
 
 
@@ -198,6 +200,26 @@ def bench_window_gqa(torch, eb, dev, steps):
     fl = acc.attention_flops(B * H * acc.visible_pairs(N, N, True, window=w), d)
     return {"swa4096_gqa32q8kv_32k_d128": {"ms": ms, "TFLOP/s": fl / ms / 1e9,
                                           "frac_mfma_peak": fl / ms / 1e9 / PEAK_BF16_TFLOPS}}
+
+
+def bench_backward(torch, eb, dev, steps):
+    """attn_bwd on the forward's shape (causal self-attention B=4, H=32, N=8192, d=128, bf16 inputs, fp32
+    gradients), o and lse from one forward outside the timed region. TFLOP/s counts the five algorithmic products
+    (2.5x the forward's FLOPs); the kernels execute seven (the dq kernel recomputes S and dP)."""
+    from workloads import normal_bf16_bits
+    from workloads import accounting as acc
+    B, H, N, d = 4, 32, 8192, 128
+    q, k, v, do = (upload_bf16(normal_bf16_bits(9, t, (B, H, N, d)), torch, dev) for t in ("q", "k", "v", "do"))
+    o, lse = eb.attn_fwd(q, k, v, causal=True)
+    dq = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+    dk, dv = torch.empty_like(dq), torch.empty_like(dq)
+    delta = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    ms = time_region(torch, lambda: eb.attn_bwd(q, k, v, o, lse, do, causal=True, dq=dq, dk=dk, dv=dv, delta=delta),
+                     max(steps, 10), 2)
+    fl = acc.attention_backward_flops(B * H * acc.visible_pairs(N, N, True), d)
+    return {"attn_bwd_causal_8k_d128": {"ms": ms, "TFLOP/s": fl / ms / 1e9,
+                                        "frac_mfma_peak": fl / ms / 1e9 / PEAK_BF16_TFLOPS,
+                                        "mfma_TFLOP/s_executed": 1.4 * fl / ms / 1e9}}
 
 
 def bench_tabular(torch, eb, dev, steps):
@@ -236,6 +258,8 @@ def main(argv=None):
                     help="also run one plain device copy of this many bytes (counter calibration)")
     ap.add_argument("--merge-only", action="store_true",
                     help="time only the LSE merge (for profiling it) and print its figures as one JSON line")
+    ap.add_argument("--bwd-only", action="store_true",
+                    help="time only the attention backward (for profiling it) and print its figures as one JSON line")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this build has no "
@@ -259,6 +283,9 @@ def main(argv=None):
         del src, dst
     if args.merge_only:
         print(json.dumps({"lse_merge_f32_inplace_1M_rows_d128": bench_merge(torch, eb, dev, args.steps)}), flush=True)
+        return 0
+    if args.bwd_only:
+        print(json.dumps(bench_backward(torch, eb, dev, args.steps)), flush=True)
         return 0
     cfg = CONFIGS["causal_8k"]
     t0 = time.perf_counter()

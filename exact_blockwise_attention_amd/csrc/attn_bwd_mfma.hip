@@ -24,6 +24,8 @@
 // (ds_read_b64_tr_b16, contraction over the rows); one XOR swizzle of the 16-byte chunks of a row keeps both
 // patterns free of bank conflicts on the 64 four-byte banks. Tiles are copied HBM -> LDS by the buffer unit
 // (buffer_load ... lds), double-buffered, one barrier per tile.
+#include <utility>
+
 #include "internal.h"
 
 namespace ebattn {
@@ -35,6 +37,8 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -76,12 +80,24 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, kRsrcWord3);
 }
 
+// min(max(x, 0), hi) for a wave-uniform x, kept in a scalar register: the vector ALU's med3 would otherwise take
+// it, and a buffer resource built from a vector register costs a loop over the lanes at every use.
+__device__ __forceinline__ int uniform_clamp(int x, int hi) {
+  return __builtin_amdgcn_readfirstlane(x < 0 ? 0 : (x > hi ? hi : x));
+}
+
 __device__ __forceinline__ float pair_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+// An empty asm statement that takes a value in and out of registers: the value counts as produced here, so the
+// optimiser cannot move its computation into a later block (it emits no instruction).
+__device__ __forceinline__ void pin(bf16x8& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(bf16x2& x) { asm volatile("" : "+v"(x)); }
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -92,7 +108,7 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 template <int D>
 __device__ __forceinline__ void copy_tile(const __bf16* X, int r0, int rows_total, char* dst, int wave, int lane) {
   using G = BG<D>;
-  const int valid = max(0, min(kBT, rows_total - r0));
+  const int valid = uniform_clamp(rows_total - r0, kBT);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(X + (int64_t)r0 * D, (int64_t)valid * G::RB);
   const int sub = lane / G::CPR, pos = lane % G::CPR;
 #pragma unroll
@@ -154,7 +170,7 @@ __device__ __forceinline__ bf16x8 tr_frag(const char* t, const Lanes<D>& la, int
 template <int D>
 __device__ __forceinline__ void load_frags(const __bf16* X, int row0, int rows_total, int lane,
                                            bf16x8 (&f)[BG<D>::KSTEPS]) {
-  const int valid = max(0, min(32, rows_total - row0));
+  const int valid = uniform_clamp(rows_total - row0, 32);
   const __amdgpu_buffer_rsrc_t r = make_rsrc(X + (int64_t)row0 * D, (int64_t)valid * D * 2);
   const int l32 = lane & 31, hi = lane >> 5;
 #pragma unroll
@@ -169,7 +185,7 @@ __device__ __forceinline__ void load_frags(const __bf16* X, int row0, int rows_t
 template <int D, bool GF32>
 __device__ __forceinline__ void store_grad(void* out, int row0, int rows_total, int lane,
                                            const f32x16 (&acc)[BG<D>::CT], float factor, bool accumulate) {
-  const int valid = max(0, min(32, rows_total - row0));
+  const int valid = uniform_clamp(rows_total - row0, 32);
   const int hi = lane >> 5, l32 = lane & 31;
   const __amdgpu_buffer_rsrc_t r =
       GF32 ? make_rsrc(reinterpret_cast<float*>(out) + (int64_t)row0 * D, (int64_t)valid * D * 4)
@@ -259,7 +275,7 @@ void attn_bwd_dq_kernel(BwdArgs a, int n_qtiles, int xcd_remap) {
   const int row = wrow0 + (lane & 31);
   float dl = 0.0f;
   {
-    const int valid = max(0, min(32, a.Nq - wrow0));
+    const int valid = uniform_clamp(a.Nq - wrow0, 32);
     if (a.o_f32) {
       const __amdgpu_buffer_rsrc_t r = make_rsrc(reinterpret_cast<const float*>(a.o) + (qbase + wrow0) * D,
                                                  (int64_t)valid * D * 4);
@@ -348,6 +364,182 @@ void attn_bwd_dq_kernel(BwdArgs a, int n_qtiles, int xcd_remap) {
   store_grad<D, GF32>(reinterpret_cast<char*>(a.dq) + qbase * D * (GF32 ? 4 : 2), wrow0, a.Nq, lane, acc, a.scale,
                       a.accumulate != 0);
 }
+
+// ------------------------------------------------------------------------------------------------------------
+// One query tile of the dk/dv kernel for one wave, laid out slot by slot: one MFMA per slot, the LDS operand
+// reads kLead slots ahead, and a scheduling fence after every slot so that the compiler keeps the order (one wave
+// per SIMD: nothing else hides the LDS latency or the vector-ALU work). With NS = 2*KSTEPS and NP = 2*CT:
+//   slots [0, NS)           S and dP of tile rows 0..31 (accumulators s0, p0)
+//   slots [NS, 2NS)         S and dP of rows 32..63 (s1, p1), beside the weights and score gradients of rows
+//                           0..31 (operand groups kk = 0, 1: rows 16*kk .. +15)
+//   slots [2NS, 2NS + 2NP)  dV += dO^T P and dK += Q^T dS for kk = 0, 1, beside the weights and score gradients
+//                           of rows 32..63 (kk = 2, 3)
+//   slots [2NS + 2NP, ...)  dV and dK for kk = 2, 3.
+// Register r of s_h / p_h holds tile row 32*h + 16*(r/8) + 8*hi + r%8: operand group kk = 2*h + r/8 and element
+// r%8 of the lane's 8 rows 16*kk + 8*hi .. +7 (whose lse and delta are read from LDS as two float4 each).
+constexpr int kLead = 3;
+
+template <int D>
+struct DkdvStage {
+  using G = BG<D>;
+  static constexpr int NS = 2 * G::KSTEPS;
+  static constexpr int NP = 2 * G::CT;
+  static constexpr int NT = 2 * NS + 4 * NP;
+  // the slot at which element E (0..31: operand group E/8, element E%8) is formed: groups 0, 1 over slots
+  // [NS + 1, 2NS), groups 2, 3 over slots [2NS + 1, 2NS + 2NP)
+  static constexpr int elem_slot(int E) {
+    return E < 16 ? NS + 1 + (E * (NS - 1)) / 16 : 2 * NS + 1 + ((E - 16) * (2 * NP - 1)) / 16;
+  }
+
+  const char* qc;
+  const char* oc;
+  const float* lc;
+  const float* dc;
+  const bf16x8 (&kf)[G::KSTEPS];
+  const bf16x8 (&vf)[G::KSTEPS];
+  f32x16 (&dk)[G::CT];
+  f32x16 (&dv)[G::CT];
+  const Lanes<D>& la;
+  float scale_log2;
+  bool masked;
+  int lo, up;
+
+  f32x16 s0, s1, p0, p1;
+  bf16x8 pb[4], sb[4];
+  float x[8], dd[8], w[8], g[8];  // per element of a group: exponent, dP - delta, weight, score gradient
+  bf16x2 wp[2][4], gp[2][4];      // completed pairs of weights and score gradients (bf16) of groups kk & 1
+  f32x4 lq[2][2], dl[2][2];       // lse (exp2 domain) and delta of groups kk (index kk & 1): the next group's
+                                  // are read while the current group's last elements are still being formed
+  bf16x8 ring[kLead + 1];
+
+  // the A operand of slot I
+  template <int I>
+  __device__ __forceinline__ bf16x8 frag() const {
+    if constexpr (I < 2 * NS) {
+      constexpr int j = I % NS;
+      return row_frag<D>((j & 1) ? oc : qc, la, I / NS, j >> 1);
+    } else {
+      constexpr int m = I - 2 * NS, j = m % NP;
+      return tr_frag<D>((j & 1) ? qc : oc, la, m / NP, j >> 1);
+    }
+  }
+
+  // Element E is formed in three steps on consecutive slots, so that no slot waits on its own results: (a) the
+  // exponent and dP - delta, (b) the exponential, (c) the score gradient, and the bf16 rounding of the group's
+  // eight weights and score gradients after its last element.
+  template <int E>
+  __device__ __forceinline__ void elem_a() {
+    constexpr int kk = E >> 3, e = E & 7, r = 8 * (kk & 1) + e;
+    const float sv = (kk >> 1) ? s1[r] : s0[r];
+    const float pv = (kk >> 1) ? p1[r] : p0[r];
+    x[e] = __builtin_fmaf(sv, scale_log2, -lq[kk & 1][e >> 2][e & 3]);
+    dd[e] = pv - dl[kk & 1][e >> 2][e & 3];
+    // pinned in this slot: the optimiser would otherwise sink the work next to its first use, past the
+    // scheduling fences and out of the MFMA shadow it is placed in
+    pin(x[e]);
+    pin(dd[e]);
+  }
+  template <int E>
+  __device__ __forceinline__ void elem_b() {
+    constexpr int e = E & 7;
+    w[e] = __builtin_amdgcn_exp2f(x[e]);
+    pin(w[e]);
+  }
+  template <int E>
+  __device__ __forceinline__ void elem_c() {
+    constexpr int kk = E >> 3, e = E & 7;
+    g[e] = w[e] * dd[e];
+    if constexpr (e & 1) {
+      // each completed pair is rounded to bf16 at once: the next group's elements reuse w and g before this
+      // group's last pair is done
+      const f32x2 xw = {w[e - 1], w[e]}, yg = {g[e - 1], g[e]};
+      wp[kk & 1][e >> 1] = __builtin_convertvector(xw, bf16x2);
+      gp[kk & 1][e >> 1] = __builtin_convertvector(yg, bf16x2);
+      pin(wp[kk & 1][e >> 1]);
+      pin(gp[kk & 1][e >> 1]);
+    } else {
+      pin(g[e]);
+    }
+    if constexpr (e == 7) {
+      const bf16x2(&a)[4] = wp[kk & 1];
+      const bf16x2(&b)[4] = gp[kk & 1];
+      pb[kk] = __builtin_shufflevector(__builtin_shufflevector(a[0], a[1], 0, 1, 2, 3),
+                                       __builtin_shufflevector(a[2], a[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+      sb[kk] = __builtin_shufflevector(__builtin_shufflevector(b[0], b[1], 0, 1, 2, 3),
+                                       __builtin_shufflevector(b[2], b[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  }
+  template <int I, int... Es>
+  __device__ __forceinline__ void elems(std::integer_sequence<int, Es...>) {
+    ((elem_slot(Es) + 2 == I ? elem_c<Es>() : void()), ...);
+    ((elem_slot(Es) + 1 == I ? elem_b<Es>() : void()), ...);
+    ((elem_slot(Es) == I ? elem_a<Es>() : void()), ...);
+  }
+
+  template <int KK>
+  __device__ __forceinline__ void read_rows() {
+    const int rb = 16 * KK + 8 * la.hi;
+    lq[KK & 1][0] = *reinterpret_cast<const f32x4*>(lc + rb);
+    lq[KK & 1][1] = *reinterpret_cast<const f32x4*>(lc + rb + 4);
+    dl[KK & 1][0] = *reinterpret_cast<const f32x4*>(dc + rb);
+    dl[KK & 1][1] = *reinterpret_cast<const f32x4*>(dc + rb + 4);
+  }
+
+  __device__ __forceinline__ void mask(f32x16& sm, int off) {
+    if (masked) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qr = off + 16 * (r >> 3) + (r & 7);
+        if (qr < lo || qr > up) sm[r] = -INFINITY;
+      }
+    }
+  }
+
+  template <int I>
+  __device__ __forceinline__ void slot() {
+    if constexpr (I + kLead < NT) ring[(I + kLead) % (kLead + 1)] = frag<I + kLead>();
+    const bf16x8 A = ring[I % (kLead + 1)];
+    if constexpr (I < 2 * NS) {
+      constexpr int h = I / NS, j = I % NS, ks = j >> 1;
+      f32x16& c = (j & 1) ? (h == 0 ? p0 : p1) : (h == 0 ? s0 : s1);
+      c = mfma(A, (j & 1) ? vf[ks] : kf[ks], ks == 0 ? f32x16{} : c);
+    } else {
+      constexpr int m = I - 2 * NS, kk = m / NP, j = m % NP, ct = j >> 1;
+      if constexpr (j & 1) dk[ct] = mfma(A, sb[kk], dk[ct]);
+      else dv[ct] = mfma(A, pb[kk], dv[ct]);
+    }
+    // lse and delta of a group, three slots before its first element
+    if constexpr (I == elem_slot(0) - 3) read_rows<0>();
+    if constexpr (I == elem_slot(8) - 3) read_rows<1>();
+    if constexpr (I == elem_slot(16) - 3) read_rows<2>();
+    if constexpr (I == elem_slot(24) - 3) read_rows<3>();
+    // the causal / window mask of a block of rows once its scores are complete (a uniform branch: only tiles
+    // that straddle an edge of the mask need it)
+    if constexpr (I == NS - 1) {
+      __builtin_amdgcn_sched_barrier(0);
+      mask(s0, 0);
+    }
+    if constexpr (I == 2 * NS - 1) {
+      __builtin_amdgcn_sched_barrier(0);
+      mask(s1, 32);
+    }
+    elems<I>(std::make_integer_sequence<int, 32>{});
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  template <int... Is>
+  __device__ __forceinline__ void run(std::integer_sequence<int, Is...>) {
+    ((ring[Is] = frag<Is>()), ...);
+  }
+  template <int... Is>
+  __device__ __forceinline__ void slots(std::integer_sequence<int, Is...>) {
+    (slot<Is>(), ...);
+  }
+  __device__ __forceinline__ void operator()() {
+    run(std::make_integer_sequence<int, kLead>{});
+    slots(std::make_integer_sequence<int, NT>{});
+  }
+};
 
 // ------------------------------------------------------------------------------------------------------------
 // dk/dv kernel: 128 keys of one key/value head per workgroup; query tiles of 64 of every query head in its group.
@@ -452,56 +644,9 @@ void attn_bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int xcd_remap) {
       if (wave == 0) load_rows(s + 1, lv, dvv);
     }
     const int i0 = (t0 + s % nt) * kBT;
-    if (i0 + kBT - 1 >= any_lo && i0 <= any_hi) {
-      f32x16 s0 = f32x16{}, s1 = f32x16{}, p0 = f32x16{}, p1 = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < G::KSTEPS; ++ks) {
-        s0 = mfma(row_frag<D>(qc, la, 0, ks), kf[ks], s0);
-        s1 = mfma(row_frag<D>(qc, la, 1, ks), kf[ks], s1);
-        p0 = mfma(row_frag<D>(oc, la, 0, ks), vf[ks], p0);
-        p1 = mfma(row_frag<D>(oc, la, 1, ks), vf[ks], p1);
-      }
-      // register r of s0/s1 holds query row 32*h + 16*(r/8) + 8*hi + r%8 of the tile (h = 0/1)
-      if (!(i0 >= all_lo && i0 + kBT - 1 <= all_hi)) {
-        const int lo = vis_lo - i0, up = vis_hi - i0;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qr = 16 * (r >> 3) + (r & 7);
-          if (qr < lo || qr > up) s0[r] = -INFINITY;
-          if (qr + 32 < lo || qr + 32 > up) s1[r] = -INFINITY;
-        }
-      }
-      bf16x8 pb[4], sb[4];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int rb = 16 * kk + 8 * hi;   // tile row of register 8*(kk&1) of block kk>>1
-        const f32x4 l0 = *reinterpret_cast<const f32x4*>(lc + rb);
-        const f32x4 l1 = *reinterpret_cast<const f32x4*>(lc + rb + 4);
-        const f32x4 e0 = *reinterpret_cast<const f32x4*>(dc + rb);
-        const f32x4 e1 = *reinterpret_cast<const f32x4*>(dc + rb + 4);
-        f32x8 x, y;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int r = 8 * (kk & 1) + e;
-          const float sv = (kk >> 1) ? s1[r] : s0[r];
-          const float pv = (kk >> 1) ? p1[r] : p0[r];
-          const float ls = e < 4 ? l0[e] : l1[e - 4];
-          const float de = e < 4 ? e0[e] : e1[e - 4];
-          const float pw = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, a.scale_log2, -ls));
-          x[e] = pw;
-          y[e] = pw * (pv - de);
-        }
-        pb[kk] = __builtin_convertvector(x, bf16x8);
-        sb[kk] = __builtin_convertvector(y, bf16x8);
-      }
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int ct = 0; ct < G::CT; ++ct) {
-          dv[ct] = mfma(tr_frag<D>(oc, la, kk, ct), pb[kk], dv[ct]);
-          dk[ct] = mfma(tr_frag<D>(qc, la, kk, ct), sb[kk], dk[ct]);
-        }
-    }
+    if (i0 + kBT - 1 >= any_lo && i0 <= any_hi)
+      DkdvStage<D>{qc, oc, lc, dc, kf, vf, dk, dv, la, a.scale_log2, !(i0 >= all_lo && i0 + kBT - 1 <= all_hi),
+                   vis_lo - i0, vis_hi - i0}();
     if (more && wave == 0) {
       ln[lane] = lv;
       dn[lane] = dvv;

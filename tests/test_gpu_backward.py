@@ -189,3 +189,23 @@ def test_backward_deterministic(eb):
     t.cuda.synchronize()
     for x, y in zip(a, b):
         assert t.equal(x, y)
+
+
+def test_backward_causal_8k_full_size_heads(eb):
+    """The backward at the forward's full workload (causal self-attention B=4, H=32, N=8192, d=128, the launch
+    the bench times: fp32 gradients): two whole (batch, head) slices against the oracle, every element."""
+    t = torch()
+    from workloads import CONFIGS
+    c = CONFIGS["causal_8k"]
+    shape = (c.B, c.H, c.Nq, c.d)
+    Q, K, V, dO = (normal_bf16_bits(c.seed, n, shape) for n in ("q", "k", "v", "do"))
+    print("[case] backward causal_8k full size", flush=True)
+    qd, kd, vd, dod = dev_bf16(Q), dev_bf16(K), dev_bf16(V), dev_bf16(dO)
+    o, lse = eb.attn_fwd(qd, kd, vd, scale=c.scale, causal=True)
+    dq, dk, dv, delta = eb.attn_bwd(qd, kd, vd, o, lse, dod, scale=c.scale, causal=True)
+    t.cuda.synchronize()
+    for b, h in ((0, 0), (3, 31)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ref = oracle.attention_backward(*(bf16_bits_to_f64(x[sl]) for x in (Q, K, V, dO)), c.scale, causal=True)
+        for name, g, r in zip(("dq", "dk", "dv", "delta"), (dq, dk, dv, delta), ref):
+            compare_grad(host_f64(g[sl]), r, f"causal_8k b{b} h{h} {name}")

@@ -39,6 +39,12 @@ def attention_flops(pairs: int, d: int) -> float:
     return 4.0 * d * pairs
 
 
+def attention_backward_flops(pairs: int, d: int) -> float:
+    """Algorithmic FLOPs of the backward over `pairs` visible (query, key) pairs: five products of 2*d FLOPs per
+    pair (S = QK^T recomputed, dP = dO V^T, dV = P^T dO, dQ = dS K, dK = dS^T Q), 2.5 times the forward."""
+    return 10.0 * d * pairs
+
+
 def tensor_bytes(n: int, d: int, elem_bytes: int) -> int:
     """Bytes of one [n, d] matrix (one head's Q, K or V)."""
     return int(n) * int(d) * int(elem_bytes)
