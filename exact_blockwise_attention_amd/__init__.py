@@ -9,6 +9,7 @@ Names and semantics follow the C ABI in include/ebattn.h:
 
     o, lse = attn_fwd(q, k, v, scale=..., causal=..., q_off=..., k_off=..., pos_stride=...)
     o, lse = attn_lse_merge(o_a, lse_a, o_b, lse_b)
+    o, lse = attn_fwd_merge(q, k, v, run_o, run_lse, ...)     # one block's attention merged in its epilogue
     dq, dk, dv, delta = attn_bwd(q, k, v, o, lse, dout, scale=..., causal=..., window=...)
     o, lse = ring_local(q_shard, [(k0, v0, k_off0), (k1, v1, k_off1), ...], scale=..., causal=..., q_off=...)
 """
@@ -65,6 +66,8 @@ def _load() -> ctypes.CDLL:
     lib.attn_fwd.restype = I
     lib.attn_fwd_ex.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, I, I64, I64, I, I64, I, I, P]
     lib.attn_fwd_ex.restype = I
+    lib.attn_fwd_merge.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, I64, I64, I, I64, I, I, P]
+    lib.attn_fwd_merge.restype = I
     lib.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, I64, I64, I, I64, I, I, I, I, P]
     lib.attn_bwd.restype = I
     lib.attn_lse_merge.argtypes = [P, P, P, P, P, P, I64, I, I, I, P]
@@ -196,6 +199,40 @@ def attn_fwd_ex(q, k, v, *, scale: Optional[float] = None, causal: bool = False,
     _check(lib.attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Hkv, Nq, Nk, d, scale,
                            int(causal), int(q_off), int(k_off), int(pos_stride), int(window), _code(q.dtype),
                            _code(out.dtype), _stream(q)))
+    return out, lse
+
+
+def attn_fwd_merge(q, k, v, run_o, run_lse, *, scale: Optional[float] = None, causal: bool = False, q_off: int = 0,
+                   k_off: int = 0, pos_stride: int = 1, window: int = 0, out=None, lse=None,
+                   out_dtype=None) -> Tuple[object, object]:
+    """attn_fwd_ex of one key/value block merged with the running fp32 result (run_o [B,H,Nq,d], run_lse
+    [B,H,Nq]) inside the attention kernel. out / lse may be run_o / run_lse themselves (in place; out fp32).
+    out_dtype defaults to float32. Returns (o, lse)."""
+    torch = _torch()
+    _need_cuda(q, k, v, run_o, run_lse, out, lse)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Hkv, Nk, d) or tuple(v.shape) != (B, Hkv, Nk, d):
+        raise ValueError("k and v must be [B, Hkv, Nk, d] with q's B and d")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share a dtype")
+    if tuple(run_o.shape) != (B, H, Nq, d) or tuple(run_lse.shape) != (B, H, Nq):
+        raise ValueError("run_o must be [B,H,Nq,d] and run_lse [B,H,Nq]")
+    if run_o.dtype != torch.float32 or run_lse.dtype != torch.float32:
+        raise TypeError("run_o and run_lse must be float32")
+    out_dtype = out_dtype or (out.dtype if out is not None else torch.float32)
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if tuple(out.shape) != (B, H, Nq, d) or tuple(lse.shape) != (B, H, Nq) or lse.dtype != torch.float32:
+        raise ValueError("out must be [B,H,Nq,d] and lse fp32 [B,H,Nq]")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _check(lib.attn_fwd_merge(_ptr(q), _ptr(k), _ptr(v), _ptr(run_o), _ptr(run_lse), _ptr(out), _ptr(lse), B, H, Hkv,
+                              Nq, Nk, d, scale, int(causal), int(q_off), int(k_off), int(pos_stride), int(window),
+                              _code(q.dtype), _code(out.dtype), _stream(q)))
     return out, lse
 
 

@@ -117,12 +117,17 @@ int check_outputs_disjoint(const void* q, const void* o, const float* lse, int64
 }
 
 // Enqueue one attention forward whose arguments have been validated.
+// With merge_o / merge_lse set (bf16 inputs only), the result is merged in the kernel's epilogue with that
+// running fp32 result; o / lse may be exactly merge_o / merge_lse. Such a launch always runs the MFMA kernel (it
+// also covers blocks that hide every key: their rows keep the running result).
 int enqueue_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t BH, int Nq, int Nk,
                 int d, float scale, int causal, int diag, int in_dtype, int o_dtype, hipStream_t stream,
-                int lo = ebattn::kNoWindow, int kv_group = 1) {
+                int lo = ebattn::kNoWindow, int kv_group = 1, const float* merge_o = nullptr,
+                const float* merge_lse = nullptr) {
   const int64_t rows = BH * Nq;
   if (rows == 0) return ATTN_OK;
-  const bool all_hidden = (Nk == 0) || (causal && (int64_t)Nq - 1 + diag < 0);
+  const bool merging = merge_o != nullptr;
+  const bool all_hidden = !merging && ((Nk == 0) || (causal && (int64_t)Nq - 1 + diag < 0));
   hipError_t e;
   if (all_hidden) {
     e = ebattn::launch_fill_empty(o, lse, rows, d, o_dtype == ATTN_F32, stream);
@@ -145,7 +150,11 @@ int enqueue_fwd(const void* q, const void* k, const void* v, void* o, float* lse
   a.diag = masks ? diag : 0;
   a.lo = masks ? lo : ebattn::kNoWindow;
   a.kv_group = kv_group;
-  if (in_dtype == ATTN_F32)
+  a.merge_o = merge_o;
+  a.merge_lse = merge_lse;
+  if (merging)
+    e = ebattn::launch_attn_fwd_bf16(a, d, o_dtype == ATTN_F32, stream);
+  else if (in_dtype == ATTN_F32)
     e = ebattn::launch_attn_fwd_f32(a, d, stream);
   else if (Nq <= ebattn::kShortMax && Nk <= ebattn::kShortMax)
     e = ebattn::launch_attn_fwd_short(a, d, o_dtype == ATTN_F32, stream);
@@ -202,6 +211,46 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
              void* stream) {
   return attn_fwd_ex(q, k, v, o, lse, B, H, H, Nq, Nk, d, scale, causal, q_off, k_off, pos_stride, 0, in_dtype,
                      o_dtype, stream);
+}
+
+int attn_fwd_merge(const void* q, const void* k, const void* v, const float* run_o, const float* run_lse, void* o,
+                   float* lse, int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal, int64_t q_off,
+                   int64_t k_off, int pos_stride, int64_t window, int in_dtype, int o_dtype, void* stream) {
+  g_err[0] = '\0';
+  int rc = check_query_side(q, o, lse, B, H, Nq, d, scale, causal, q_off, pos_stride, in_dtype, o_dtype);
+  if (rc != ATTN_OK) return rc;
+  if (in_dtype != ATTN_BF16) return fail(ATTN_EUNSUPPORTED, "attn_fwd_merge takes bf16 q, k, v");
+  if (H > 0 && (Hkv < 1 || Hkv > H || H % Hkv != 0))
+    return fail(ATTN_EINVAL, "Hkv=%d must divide H=%d", Hkv, H);
+  if (window < 0) return fail(ATTN_EINVAL, "window must be >= 0 (got %lld)", (long long)window);
+  if (window > 0 && !causal) return fail(ATTN_EINVAL, "a sliding window requires causal = 1");
+  if (window > kOffLimit) return fail(ATTN_EINVAL, "window out of range");
+  const int64_t BH = (int64_t)B * H;
+  const int64_t rows = BH * Nq;
+  rc = check_kv(k, v, (int64_t)B * (H > 0 ? Hkv : 0), Nk, d, in_dtype, k_off, q, o, lse, Nq, o_dtype, BH);
+  if (rc != ATTN_OK) return rc;
+  if (rows == 0) return ATTN_OK;
+  if (!run_o || !run_lse) return fail(ATTN_EINVAL, "null run_o or run_lse");
+  if (!aligned(run_o, 16) || !aligned(run_lse, 4)) return fail(ATTN_EINVAL, "run_o / run_lse misaligned");
+  rc = check_outputs_disjoint(q, o, lse, rows, d, in_dtype, o_dtype);
+  if (rc != ATTN_OK) return rc;
+  // o may be exactly run_o (fp32 output), lse exactly run_lse; any other overlap is an error
+  const Span sro = span(run_o, rows * d * 4), srl = span(run_lse, rows * 4);
+  const Span so = span(o, rows * d * elem_bytes(o_dtype)), sl = span(lse, rows * 4);
+  const bool o_in_place = (o == (const void*)run_o) && o_dtype == ATTN_F32;
+  const bool l_in_place = (lse == run_lse);
+  if ((!o_in_place && overlap(so, sro)) || (!l_in_place && overlap(sl, srl)) || overlap(so, srl) ||
+      overlap(sl, sro) || overlap(sro, srl))
+    return fail(ATTN_EINVAL, "o / lse overlap run_o / run_lse other than exactly in place");
+  const int64_t qb = rows * d * 2, kvb = (int64_t)B * (H > 0 ? Hkv : 0) * Nk * d * 2;
+  if (overlap(sro, span(q, qb)) || overlap(srl, span(q, qb)) ||
+      (Nk > 0 && (overlap(sro, span(k, kvb)) || overlap(sro, span(v, kvb)) || overlap(srl, span(k, kvb)) ||
+                  overlap(srl, span(v, kvb)))))
+    return fail(ATTN_EINVAL, "run_o / run_lse overlap q, k or v");
+  (void)hipGetLastError();
+  return enqueue_fwd(q, k, v, o, lse, BH, Nq, Nk, d, scale, causal, diag_offset(q_off, k_off, pos_stride), in_dtype,
+                     o_dtype, reinterpret_cast<hipStream_t>(stream), window_lo(q_off, k_off, pos_stride, window),
+                     H > 0 ? H / Hkv : 1, run_o, run_lse);
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
@@ -413,6 +462,22 @@ int ring_local(const void* q_shard, const attn_kv_block* kv_blocks, int n_blocks
   float* part_l = reinterpret_cast<float*>(ws + 2 * align256(rows * d * 4) + align256(rows * 4));
 
   int done = 0;
+  if (in_dtype == ATTN_BF16) {
+    // bf16 inputs: every block after the first merges into the running fp32 result in the attention kernel's
+    // epilogue (no partial buffer, no separate merge pass); the last block writes o and lse
+    for (int i = 0; i < n_blocks; ++i) {
+      const attn_kv_block& b = kv_blocks[i];
+      if (classify(Nq, b.Nk, causal, q_off, b.k_off, pos_stride) == 0) continue;
+      const int diag = diag_offset(q_off, b.k_off, pos_stride);
+      const bool last = (done == live - 1);
+      rc = enqueue_fwd(q_shard, b.k, b.v, last ? o : acc_o, last ? lse : acc_l, BH, Nq, b.Nk, d, scale, causal, diag,
+                       in_dtype, last ? o_dtype : ATTN_F32, st, ebattn::kNoWindow, 1, done > 0 ? acc_o : nullptr,
+                       done > 0 ? acc_l : nullptr);
+      if (rc != ATTN_OK) return rc;
+      ++done;
+    }
+    return ATTN_OK;
+  }
   for (int i = 0; i < n_blocks; ++i) {
     const attn_kv_block& b = kv_blocks[i];
     if (classify(Nq, b.Nk, causal, q_off, b.k_off, pos_stride) == 0) continue;

@@ -460,20 +460,52 @@ __device__ __forceinline__ void load_q(const __bf16* Qblk, int rows_valid, int r
 // Epilogue: O = acc / lq, lse = ln2 * (m + log2 l); a row with no visible key gives (0, -inf). Register r of O^T
 // tile ct holds head-dim column 32*ct + 8*(r/4) + 4*hi + r%4 of this lane's row; the buffer range of the
 // workgroup's block drops the stores of rows past Nq.
-template <int D, bool OF32>
+// With MERGE the row is first merged with the running result (merge_o, merge_lse) by the log-sum-exp rule of
+// "分布式注意力机制突破：长序列处理的全景技术架构与实践指南" §3.4 (common maximum, parts weighted by exp(lse_i - lse)):
+// both lanes of the row read its running lse and their halves of its running o before either writes, so the
+// output may alias the running result.
+template <int D, bool OF32, bool MERGE>
 __device__ __forceinline__ void store_out(const FwdArgs& a, int64_t bh, int q0, int block_rows, int local_row, int lane,
                                           const f32x16 (&acc)[Geom<D>::CT], float m_ref, float l_run, float lq_run) {
   using G = Geom<D>;
   const int hi = lane >> 5;
   const float l_tot = pair_sum(l_run);
   const float lq_tot = pair_sum(lq_run);
-  const float inv = lq_tot > 0.0f ? 1.0f / lq_tot : 0.0f;
+  float inv = lq_tot > 0.0f ? 1.0f / lq_tot : 0.0f;
   const int qi = q0 + local_row;
-  if (hi == 0 && qi < a.Nq)
-    a.lse[bh * (int64_t)a.Nq + qi] =
-        l_tot > 0.0f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f : -INFINITY;
   const int64_t o_rows = min(block_rows, a.Nq - q0);
   const int64_t base = (bh * (int64_t)a.Nq + q0) * D;
+  float lse_out = l_tot > 0.0f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f : -INFINITY;
+  float f_run = 0.0f;                    // weight of the running o in the merged row
+  f32x4 run[G::CT][4];                   // this lane's half of the running o
+  if constexpr (MERGE) {
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.merge_o + base, o_rows * D * 4);
+#pragma unroll
+    for (int ct = 0; ct < G::CT; ++ct)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = ct * 32 + 8 * g + 4 * hi;
+        run[ct][g] = c < D ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                       rr, (uint32_t)((local_row * D + c) * 4), 0, 0))
+                           : f32x4{};
+      }
+    const float l_prev = qi < a.Nq ? a.merge_lse[bh * (int64_t)a.Nq + qi] : -INFINITY;
+    // log2-domain merge of the two parts; an empty part (lse = -inf) weighs zero, two empty parts give (0, -inf)
+    const float p2 = l_prev * 1.4426950408889634f;
+    const float b2 = l_tot > 0.0f ? m_ref + __builtin_amdgcn_logf(l_tot) : -INFINITY;
+    const float m2 = __builtin_fmaxf(p2, b2);
+    if (m2 == -INFINITY) {
+      lse_out = -INFINITY;
+      inv = 0.0f;
+    } else {
+      const float wp = __builtin_amdgcn_exp2f(p2 - m2), wb = __builtin_amdgcn_exp2f(b2 - m2);
+      const float rs = 1.0f / (wp + wb);
+      lse_out = (m2 + __builtin_amdgcn_logf(wp + wb)) * 0.69314718055994531f;
+      f_run = wp * rs;
+      inv *= wb * rs;
+    }
+  }
+  if (hi == 0 && qi < a.Nq) a.lse[bh * (int64_t)a.Nq + qi] = lse_out;
   const __amdgpu_buffer_rsrc_t ro = OF32 ? make_rsrc(reinterpret_cast<float*>(a.o) + base, o_rows * D * 4)
                                          : make_rsrc(reinterpret_cast<__bf16*>(a.o) + base, o_rows * D * 2);
 #pragma unroll
@@ -482,8 +514,9 @@ __device__ __forceinline__ void store_out(const FwdArgs& a, int64_t bh, int q0, 
     for (int g = 0; g < 4; ++g) {
       const int c = ct * 32 + 8 * g + 4 * hi;
       if (c >= D) continue;
-      const f32x4 y = {acc[ct][4 * g] * inv, acc[ct][4 * g + 1] * inv, acc[ct][4 * g + 2] * inv,
-                       acc[ct][4 * g + 3] * inv};
+      f32x4 y = {acc[ct][4 * g] * inv, acc[ct][4 * g + 1] * inv, acc[ct][4 * g + 2] * inv,
+                 acc[ct][4 * g + 3] * inv};
+      if constexpr (MERGE) y += f_run * run[ct][g];
       if (OF32)
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, y), ro, (uint32_t)((local_row * D + c) * 4), 0, 0);
       else
@@ -516,7 +549,7 @@ constexpr bool pipelined() { return D == 128; }
 // without a causal mask, 8 (256 rows, one workgroup per CU: each K/V tile is copied into LDS once per 256 rows
 // instead of once per 128; under a causal mask the waves of such a block finish too unevenly for it to pay).
 
-template <int D, bool OF32, int NW>
+template <int D, bool OF32, int NW, bool MERGE>
 __global__ __launch_bounds__(64 * NW)
 __attribute__((amdgpu_waves_per_eu(waves_per_simd<D>(), waves_per_simd<D>())))
 void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
@@ -662,7 +695,7 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
       if (t + 1 < ntiles) step(t + 1, k1, v1, k0, v0);
     }
   }
-  store_out<D, OF32>(a, bh, q0, kRows, wave * 32 + (lane & 31), lane, acc, m_ref, l_run, lq_run);
+  store_out<D, OF32, MERGE>(a, bh, q0, kRows, wave * 32 + (lane & 31), lane, acc, m_ref, l_run, lq_run);
 }
 
 template <int D, bool OF32, int NW>
@@ -672,8 +705,12 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
   const int64_t total = (int64_t)n_qtiles * a.BH;
   if (total > 0x7fffffff) return hipErrorInvalidConfiguration;
   const int remap = (total % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, OF32, NW>), dim3((unsigned)total), dim3(64 * NW), 0, stream, a, n_qtiles,
-                     remap);
+  if (a.merge_o)
+    hipLaunchKernelGGL((attn_fwd_kernel<D, OF32, NW, true>), dim3((unsigned)total), dim3(64 * NW), 0, stream, a,
+                       n_qtiles, remap);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<D, OF32, NW, false>), dim3((unsigned)total), dim3(64 * NW), 0, stream, a,
+                       n_qtiles, remap);
   return hipGetLastError();
 }
 

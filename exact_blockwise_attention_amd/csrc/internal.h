@@ -30,9 +30,15 @@ struct FwdArgs {
   int diag;
   int lo;
   int kv_group;
+  // Optional running result to merge with (bf16 MFMA path only; null otherwise): fp32 o [BH, Nq, d] and lse
+  // [BH, Nq] of the same query rows over other keys. The kernel then writes the log-sum-exp merge of that running
+  // result and its own in place of its own; o may alias merge_o (fp32 output) and lse may alias merge_lse.
+  const float* merge_o;
+  const float* merge_lse;
 };
 
-// bf16 operands on MFMA; d in {24, 64, 128}; o is bf16 (o_f32 = 0) or fp32 (o_f32 = 1).
+// bf16 operands on MFMA; d in {24, 64, 128}; o is bf16 (o_f32 = 0) or fp32 (o_f32 = 1); merges with
+// (merge_o, merge_lse) when they are set.
 hipError_t launch_attn_fwd_bf16(const FwdArgs& a, int d, int o_f32, hipStream_t stream);
 // fp32 operands and output on the vector ALU (the fp32 correctness path); d in {24, 64, 128}.
 hipError_t launch_attn_fwd_f32(const FwdArgs& a, int d, hipStream_t stream);

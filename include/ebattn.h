@@ -91,6 +91,23 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
                 int64_t q_off, int64_t k_off, int pos_stride, int64_t window, int in_dtype, int o_dtype,
                 void* stream);
 
+/* attn_fwd_merge -- attention of one key/value block merged into a running result in the same kernel: the
+ * "accumulate each received block" step of "Mosaic多轴注意力分片：突破Transformer长序列处理瓶颈" §3.2, with the
+ * log-sum-exp merge of "分布式注意力机制突破：长序列处理的全景技术架构与实践指南" §3.4 done in the attention
+ * kernel's epilogue (no partial result in memory, no separate merge pass).
+ *   (o, lse) = merge((run_o, run_lse), attn_fwd_ex(q, k, v, ...)), i.e. lse = log(exp(run_lse) + exp(lse_blk)),
+ *   o = exp(run_lse - lse) * run_o + exp(lse_blk - lse) * o_blk; a part with lse = -inf weighs zero.
+ *   run_o       fp32 [B,H,Nq,d] and run_lse fp32 [B,H,Nq]: the running result over other keys (device pointers).
+ *   In place    o may be exactly run_o (o_dtype ATTN_F32) and lse exactly run_lse; any other overlap of o, lse,
+ *               run_o, run_lse, q, k, v is ATTN_EINVAL.
+ *   in_dtype    ATTN_BF16 only (ATTN_EUNSUPPORTED otherwise); d in {24, 64, 128}.
+ *   A block that hides every key (or Nk = 0) leaves the running result unchanged (copied to o, lse).
+ *   Everything else, errors included, as attn_fwd_ex. */
+int attn_fwd_merge(const void* q, const void* k, const void* v, const float* run_o, const float* run_lse,
+                   void* o, float* lse, int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                   int64_t q_off, int64_t k_off, int pos_stride, int64_t window, int in_dtype, int o_dtype,
+                   void* stream);
+
 /* attn_bwd -- gradients of exact attention (the backward pass of attn_fwd_ex), with the attention weights
  * recomputed tile by tile from the saved lse instead of stored ("深度学习注意力机制优化与FlashAttention实践"
  * §4.1 item 3 and §3.3). For an output gradient dout = dL/do:
@@ -143,9 +160,11 @@ typedef struct {
 /* ring_local -- one device's share of Ring Attention: q_shard [B,H,Nq,d] against kv_blocks[0..n_blocks-1],
  * processed in the given order (the order the blocks would arrive around the ring). Blocks that hide every
  * key from every query row (causal) are skipped without a launch. The first live block's attention goes to
- * the fp32 accumulator in the workspace, every later block's to a second fp32 partial that is merged into the
- * accumulator; the last merge writes o (o_dtype) and lse. A single live block writes o and lse directly; no
- * live block writes (0, -inf) rows. The result equals attention over the union of the blocks.
+ * the fp32 accumulator in the workspace. With bf16 inputs every later block is merged into that accumulator
+ * inside its attention kernel (as attn_fwd_merge), the last one writing o (o_dtype) and lse; with fp32 inputs
+ * every later block goes to a second fp32 partial in the workspace that attn_lse_merge folds into the
+ * accumulator, the last merge writing o and lse. A single live block writes o and lse directly; no live block
+ * writes (0, -inf) rows. The result equals attention over the union of the blocks.
  *   workspace   device buffer of at least ring_local_workspace_bytes(B, H, Nq, d) bytes, 256-byte aligned,
  *               not overlapping anything else; may be NULL only if at most one block is live.
  *   Other arguments as attn_fwd. */
@@ -153,8 +172,8 @@ int ring_local(const void* q_shard, const attn_kv_block* kv_blocks, int n_blocks
                int B, int H, int Nq, int d, float scale, int causal, int64_t q_off, int pos_stride,
                int in_dtype, int o_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace ring_local needs: two fp32 (o, lse) buffers of B*H*Nq rows, each 256-byte aligned.
- * Returns 0 for negative sizes. */
+/* Bytes of workspace ring_local needs: two fp32 (o, lse) buffers of B*H*Nq rows, each 256-byte aligned (the
+ * second is used with fp32 inputs only). Returns 0 for negative sizes. */
 size_t ring_local_workspace_bytes(int B, int H, int Nq, int d);
 
 /* ring_local_plan -- host-only classification of each block, exactly as ring_local decides it (no device

@@ -261,3 +261,38 @@ def test_attn_bwd_zero_sized_calls_are_noops():
     assert bwd(B=0, q=None, k=None, v=None, o=None, lse=None, do=None, dq=None, dk=None, dv=None, delta=None) == eb.ATTN_OK
     # with Nq = 0 the query-side pointers are not needed, but dk and dv still are
     assert bwd(Nq=0, dk=None) == eb.ATTN_EINVAL
+
+
+def fwd_merge(**kw):
+    args = dict(q=A, k=A + B16, v=A + 2 * B16, ro=A + 3 * B16, rl=A + 4 * B16, o=A + 5 * B16, lse=A + 6 * B16, B=1,
+                H=8, Hkv=2, Nq=64, Nk=64, d=128, scale=0.125, causal=1, q_off=0, k_off=0, stride=1, window=0,
+                it=eb.ATTN_BF16, ot=eb.ATTN_F32, stream=None)
+    args.update(kw)
+    return lib.attn_fwd_merge(args["q"], args["k"], args["v"], args["ro"], args["rl"], args["o"], args["lse"],
+                              args["B"], args["H"], args["Hkv"], args["Nq"], args["Nk"], args["d"], args["scale"],
+                              args["causal"], args["q_off"], args["k_off"], args["stride"], args["window"], args["it"],
+                              args["ot"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ro=None), eb.ATTN_EINVAL),
+    (dict(rl=None), eb.ATTN_EINVAL),
+    (dict(ro=A + 3 * B16 + 4), eb.ATTN_EINVAL),                  # misaligned running o
+    (dict(it=eb.ATTN_F32), eb.ATTN_EUNSUPPORTED),                 # bf16 inputs only
+    (dict(Hkv=3), eb.ATTN_EINVAL),
+    (dict(window=4, causal=0), eb.ATTN_EINVAL),
+    (dict(o=A + 3 * B16, ot=eb.ATTN_BF16), eb.ATTN_EINVAL),     # in place needs an fp32 output
+    (dict(o=A + 3 * B16 + 1024), eb.ATTN_EINVAL),                # o overlaps run_o without being it
+    (dict(lse=A + 4 * B16 + 8), eb.ATTN_EINVAL),                 # lse overlaps run_lse without being it
+    (dict(rl=A + 3 * B16 + 4096), eb.ATTN_EINVAL),               # run_lse inside run_o
+    (dict(ro=A + B16), eb.ATTN_EINVAL),                          # run_o over k
+    (dict(d=32), eb.ATTN_EUNSUPPORTED),
+])
+def test_attn_fwd_merge_validation(kw, code):
+    assert fwd_merge(**kw) == code
+    assert eb.last_error() != ""
+
+
+def test_attn_fwd_merge_zero_sized():
+    assert fwd_merge(B=0) == eb.ATTN_OK
+    assert fwd_merge(Nq=0, ro=None, rl=None) == eb.ATTN_OK
