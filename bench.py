@@ -152,6 +152,7 @@ def bench_extra(torch, eb, dev, steps):
                                                   workspace=ws), max(2, steps // 4), 1)
     fl = acc.attention_flops(acc.config_pairs(c3), c3.d)
     out["ring_local_rank2of4_128k"] = {"ms": ms, "TFLOP/s": fl / ms / 1e9, "frac_mfma_peak": fl / ms / 1e9 / PEAK_BF16_TFLOPS}
+    out["ring_pipelined_rank2of4_128k_h2d"] = bench_ring_pipeline(torch, eb, dev, c3, qd, kd, vd, order, ms, fl, steps)
     del qd, kd, vd, blocks, ws, o, lse
     torch.cuda.empty_cache()
     # striped: all four query stripes of N = 65536, H = 16
@@ -182,6 +183,36 @@ def bench_extra(torch, eb, dev, steps):
     torch.cuda.empty_cache()
     out.update(bench_backward(torch, eb, dev, steps))
     return out
+
+
+def bench_ring_pipeline(torch, eb, dev, c3, qd, kd, vd, order, ms_compute, fl, steps):
+    """The ring share with its exchange step on this GPU (ring_local_pipelined): the resident block is read in
+    place, every incoming live block is copied from pinned host memory (the stand-in for the neighbour's link;
+    over PCIe, by the copy engines) into a receive slot on a second stream while the compute stream attends the
+    block before it. Reported beside the compute alone (ring_local, all blocks resident) and the copies alone:
+    hidden = (compute + copies - pipelined) / copies is the share of the transfer time hidden under compute."""
+    n = c3.Nq
+    live = [s for s in order if s * n <= c3.q_off + n - 1]            # blocks a causal share sees at all
+    host = {s: (kd[s].cpu().pin_memory(), vd[s].cpu().pin_memory()) for s in live[1:]}
+    blocks = [(kd[live[0]], vd[live[0]], live[0] * n)] + [(host[s][0], host[s][1], s * n) for s in live[1:]]
+    ws = torch.empty(eb.ring_local_pipelined_workspace_bytes(c3.B, c3.H, n, c3.d, n), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(qd)
+    lse = torch.empty((c3.B, c3.H, n), dtype=torch.float32, device=dev)
+    cstream = torch.cuda.Stream(device=dev)
+    ms_pipe = time_region(torch, lambda: eb.ring_local_pipelined(qd, blocks, causal=True, q_off=c3.q_off, out=o, lse=lse,
+                                                                 workspace=ws, copy_stream=cstream),
+                          max(2, steps // 4), 1)
+    recv = [torch.empty_like(kd[0]) for _ in range(2)]
+
+    def copies():
+        for s in live[1:]:
+            recv[0].copy_(host[s][0], non_blocking=True)
+            recv[1].copy_(host[s][1], non_blocking=True)
+    ms_copy = time_region(torch, copies, max(2, steps // 4), 1)
+    nbytes = sum(host[s][0].numel() * 2 * 2 for s in live[1:])
+    return {"ms": ms_pipe, "TFLOP/s": fl / ms_pipe / 1e9, "ms_compute_only": ms_compute, "ms_copies_only": ms_copy,
+            "copy_GB/s": nbytes / ms_copy / 1e6, "bytes_copied": nbytes,
+            "hidden_fraction_of_copies": (ms_compute + ms_copy - ms_pipe) / ms_copy}
 
 
 def bench_window_gqa(torch, eb, dev, steps):

@@ -12,6 +12,7 @@ Names and semantics follow the C ABI in include/ebattn.h:
     o, lse = attn_fwd_merge(q, k, v, run_o, run_lse, ...)     # one block's attention merged in its epilogue
     dq, dk, dv, delta = attn_bwd(q, k, v, o, lse, dout, scale=..., causal=..., window=...)
     o, lse = ring_local(q_shard, [(k0, v0, k_off0), (k1, v1, k_off1), ...], scale=..., causal=..., q_off=...)
+    o, lse = ring_local_pipelined(q_shard, blocks, ..., copy_stream=s)   # incoming blocks copied while computing
 """
 from __future__ import annotations
 
@@ -76,6 +77,10 @@ def _load() -> ctypes.CDLL:
     lib.ring_local.restype = I
     lib.ring_local_workspace_bytes.argtypes = [I, I, I, I]
     lib.ring_local_workspace_bytes.restype = SZ
+    lib.ring_local_pipelined.argtypes = [P, ctypes.POINTER(KVBlock), I, P, P, I, I, I, I, F, I, I64, I, I, P, SZ, P, P]
+    lib.ring_local_pipelined.restype = I
+    lib.ring_local_pipelined_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.ring_local_pipelined_workspace_bytes.restype = SZ
     lib.ring_local_plan.argtypes = [ctypes.POINTER(KVBlock), I, I, I, I64, I, ctypes.POINTER(I)]
     lib.ring_local_plan.restype = I
     lib.attn_last_error.argtypes = []
@@ -371,4 +376,53 @@ def ring_local(q_shard, kv_blocks, *, scale: Optional[float] = None, causal: boo
     _check(lib.ring_local(_ptr(q_shard), arr, n, _ptr(out), _ptr(lse), B, H, Nq, d, scale, int(causal), int(q_off),
                           int(pos_stride), _code(q_shard.dtype), _code(out.dtype), ws_ptr, ws_bytes,
                           _stream(q_shard)))
+    return out, lse
+
+
+def ring_local_pipelined_workspace_bytes(B: int, H: int, Nq: int, d: int, Nk_max: int) -> int:
+    return int(lib.ring_local_pipelined_workspace_bytes(B, H, Nq, d, Nk_max))
+
+
+def ring_local_pipelined(q_shard, kv_blocks, *, scale: Optional[float] = None, causal: bool = False, q_off: int = 0,
+                         pos_stride: int = 1, out=None, lse=None, out_dtype=None, workspace=None,
+                         copy_stream=None) -> Tuple[object, object]:
+    """ring_local with the ring's exchange step on this device: kv_blocks[0] = (k, v, k_off) is resident (a GPU
+    tensor); every later block is copied into a receive slot on `copy_stream` while the current torch stream
+    attends the block before it. Incoming k, v may be pinned CPU tensors (the stand-in for the link) or GPU
+    tensors. bf16 only. copy_stream: a torch.cuda.Stream of default priority (one is created when None)."""
+    torch = _torch()
+    _need_cuda(q_shard, out, lse, workspace)
+    if q_shard.dim() != 4:
+        raise ValueError("q_shard must be [B, H, Nq, d]")
+    B, H, Nq, d = q_shard.shape
+    if q_shard.dtype != torch.bfloat16:
+        raise TypeError("ring_local_pipelined takes bf16 tensors")
+    for i, (k, v, _) in enumerate(kv_blocks):
+        if k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+            raise TypeError("blocks must be bf16")
+        if not (k.is_contiguous() and v.is_contiguous()):
+            raise ValueError("blocks must be contiguous")
+        if i == 0 and not (k.is_cuda and v.is_cuda):
+            raise ValueError("block 0 is read in place and must be on the GPU")
+        if not k.is_cuda and not (k.is_pinned() and v.is_pinned()):
+            raise ValueError("a CPU block must be in pinned memory")
+        if tuple(k.shape) != (B, H, k.shape[2], d) or tuple(v.shape) != tuple(k.shape):
+            raise ValueError("each block must be [B, H, Nk, d] matching q_shard")
+    out_dtype = out_dtype or (out.dtype if out is not None else q_shard.dtype)
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=out_dtype, device=q_shard.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q_shard.device)
+    nk_max = max([k.shape[2] for k, _, _ in kv_blocks[1:]] or [0])
+    need = ring_local_pipelined_workspace_bytes(B, H, Nq, d, nk_max)
+    if workspace is None and len(kv_blocks) > 1:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_shard.device)
+    if copy_stream is None:
+        copy_stream = torch.cuda.Stream(device=q_shard.device)
+    arr, n = _blocks(kv_blocks)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.ring_local_pipelined(_ptr(q_shard), arr, n, _ptr(out), _ptr(lse), B, H, Nq, d, scale, int(causal),
+                                    int(q_off), int(pos_stride), _code(out.dtype), _ptr(workspace), ws_bytes,
+                                    _stream(q_shard), copy_stream.cuda_stream))
     return out, lse

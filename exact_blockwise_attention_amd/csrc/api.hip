@@ -506,4 +506,146 @@ int ring_local(const void* q_shard, const attn_kv_block* kv_blocks, int n_blocks
   return ATTN_OK;
 }
 
+size_t ring_local_pipelined_workspace_bytes(int B, int H, int Nq, int d, int Nk_max) {
+  if (B < 0 || H < 0 || Nq < 0 || d < 0 || Nk_max < 0) return 0;
+  const size_t rows = (size_t)B * H * Nq, kv = (size_t)B * H * Nk_max * d * 2;
+  return align256(rows * d * 4) + align256(rows * 4) + 4 * align256(kv);
+}
+
+int ring_local_pipelined(const void* q_shard, const attn_kv_block* kv_blocks, int n_blocks, void* o, float* lse,
+                         int B, int H, int Nq, int d, float scale, int causal, int64_t q_off, int pos_stride,
+                         int o_dtype, void* workspace, size_t workspace_bytes, void* compute_stream,
+                         void* copy_stream) {
+  g_err[0] = '\0';
+  int rc = check_query_side(q_shard, o, lse, B, H, Nq, d, scale, causal, q_off, pos_stride, ATTN_BF16, o_dtype);
+  if (rc != ATTN_OK) return rc;
+  if (n_blocks < 0) return fail(ATTN_EINVAL, "negative n_blocks");
+  if (n_blocks > 0 && !kv_blocks) return fail(ATTN_EINVAL, "null kv_blocks");
+  const int64_t BH = (int64_t)B * H;
+  const int64_t rows = BH * Nq;
+  int nk_max = 0;
+  for (int i = 0; i < n_blocks; ++i) {
+    rc = check_kv(kv_blocks[i].k, kv_blocks[i].v, BH, kv_blocks[i].Nk, d, ATTN_BF16, kv_blocks[i].k_off, q_shard, o,
+                  lse, Nq, o_dtype, BH);
+    if (rc != ATTN_OK) {
+      char msg[512];
+      snprintf(msg, sizeof(msg), "block %d: %s", i, g_err);
+      return fail(rc, "%s", msg);
+    }
+    if (i > 0 && kv_blocks[i].Nk > nk_max) nk_max = kv_blocks[i].Nk;
+  }
+  if (rows == 0) return ATTN_OK;
+  rc = check_outputs_disjoint(q_shard, o, lse, rows, d, ATTN_BF16, o_dtype);
+  if (rc != ATTN_OK) return rc;
+  // live blocks, in ring order; block 0 is resident, every later one arrives through a receive slot
+  int live = 0, incoming = 0;
+  for (int i = 0; i < n_blocks; ++i) {
+    const bool l = classify(Nq, kv_blocks[i].Nk, causal, q_off, kv_blocks[i].k_off, pos_stride) != 0;
+    live += l;
+    incoming += l && i > 0;
+  }
+  const size_t need = ring_local_pipelined_workspace_bytes(B, H, Nq, d, nk_max);
+  if (live >= 2 || incoming > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(ATTN_EWORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 256)) return fail(ATTN_EINVAL, "workspace must be 256-byte aligned");
+    const Span sw = span(workspace, (int64_t)need);
+    if (overlap(sw, span(o, rows * d * elem_bytes(o_dtype))) || overlap(sw, span(lse, rows * 4)) ||
+        overlap(sw, span(q_shard, rows * d * 2)))
+      return fail(ATTN_EINVAL, "workspace overlaps q, o or lse");
+    for (int i = 0; i < n_blocks; ++i) {
+      const int64_t kvb = BH * kv_blocks[i].Nk * d * 2;
+      if (kv_blocks[i].Nk > 0 && (overlap(sw, span(kv_blocks[i].k, kvb)) || overlap(sw, span(kv_blocks[i].v, kvb))))
+        return fail(ATTN_EINVAL, "workspace overlaps block %d", i);
+    }
+  }
+  const hipStream_t cs = reinterpret_cast<hipStream_t>(compute_stream);
+  const hipStream_t xs = reinterpret_cast<hipStream_t>(copy_stream);
+  (void)hipGetLastError();
+  if (live == 0) {
+    const hipError_t e = ebattn::launch_fill_empty(o, lse, rows, d, o_dtype == ATTN_F32, cs);
+    return e == hipSuccess ? ATTN_OK : hip_fail(e, "fill launch");
+  }
+  char* ws = reinterpret_cast<char*>(workspace);
+  float* acc_o = reinterpret_cast<float*>(ws);
+  float* acc_l = reinterpret_cast<float*>(ws + align256(rows * d * 4));
+  char* slots = ws + align256(rows * d * 4) + align256(rows * 4);
+  const size_t kv_slot = align256((size_t)BH * nk_max * d * 2);
+  auto slot_k = [&](int s) { return slots + (2 * s) * kv_slot; };
+  auto slot_v = [&](int s) { return slots + (2 * s + 1) * kv_slot; };
+
+  // Two receive slots: while the compute stream attends the block in one slot, the copy stream brings the next
+  // incoming block into the other. ready[s]: slot s holds its block; freed[s]: the compute that read slot s is
+  // done, so the slot may be overwritten.
+  hipEvent_t ready[2] = {nullptr, nullptr}, freed[2] = {nullptr, nullptr};
+  hipError_t e = hipSuccess;
+  for (int s = 0; s < 2 && e == hipSuccess; ++s) {
+    e = hipEventCreateWithFlags(&ready[s], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&freed[s], hipEventDisableTiming);
+  }
+  auto release = [&]() {
+    for (int s = 0; s < 2; ++s) {
+      if (ready[s]) (void)hipEventDestroy(ready[s]);
+      if (freed[s]) (void)hipEventDestroy(freed[s]);
+    }
+  };
+  if (e != hipSuccess) {
+    release();
+    return hip_fail(e, "event create");
+  }
+  int inc[ATTN_MAX_RING_BLOCKS];
+  int n_inc = 0;
+  for (int i = 1; i < n_blocks; ++i)
+    if (classify(Nq, kv_blocks[i].Nk, causal, q_off, kv_blocks[i].k_off, pos_stride) != 0) {
+      if (n_inc == ATTN_MAX_RING_BLOCKS) {
+        release();
+        return fail(ATTN_EINVAL, "more than %d live incoming blocks", ATTN_MAX_RING_BLOCKS);
+      }
+      inc[n_inc++] = i;
+    }
+  auto copy_in = [&](int j) -> hipError_t {
+    const attn_kv_block& b = kv_blocks[inc[j]];
+    const int s = j & 1;
+    hipError_t r = hipSuccess;
+    if (j >= 2) r = hipStreamWaitEvent(xs, freed[s], 0);   // the block two steps back has been consumed
+    const size_t bytes = (size_t)BH * b.Nk * d * 2;
+    if (r == hipSuccess) r = hipMemcpyAsync(slot_k(s), b.k, bytes, hipMemcpyDefault, xs);
+    if (r == hipSuccess) r = hipMemcpyAsync(slot_v(s), b.v, bytes, hipMemcpyDefault, xs);
+    if (r == hipSuccess) r = hipEventRecord(ready[s], xs);
+    return r;
+  };
+  int done = 0;
+  auto attend = [&](const void* k, const void* v, const attn_kv_block& b) -> int {
+    const bool last = (done == live - 1);
+    const int r = enqueue_fwd(q_shard, k, v, last ? o : acc_o, last ? lse : acc_l, BH, Nq, b.Nk, d, scale, causal,
+                              diag_offset(q_off, b.k_off, pos_stride), ATTN_BF16, last ? o_dtype : ATTN_F32, cs,
+                              ebattn::kNoWindow, 1, done > 0 ? acc_o : nullptr, done > 0 ? acc_l : nullptr);
+    ++done;
+    return r;
+  };
+  if (n_inc > 0) e = copy_in(0);
+  if (e == hipSuccess && n_blocks > 0 &&
+      classify(Nq, kv_blocks[0].Nk, causal, q_off, kv_blocks[0].k_off, pos_stride) != 0) {
+    rc = attend(kv_blocks[0].k, kv_blocks[0].v, kv_blocks[0]);
+    if (rc != ATTN_OK) {
+      release();
+      return rc;
+    }
+  }
+  for (int j = 0; j < n_inc && e == hipSuccess; ++j) {
+    if (j + 1 < n_inc) e = copy_in(j + 1);
+    if (e == hipSuccess) e = hipStreamWaitEvent(cs, ready[j & 1], 0);
+    if (e != hipSuccess) break;
+    rc = attend(slot_k(j & 1), slot_v(j & 1), kv_blocks[inc[j]]);
+    if (rc != ATTN_OK) {
+      release();
+      return rc;
+    }
+    e = hipEventRecord(freed[j & 1], cs);
+  }
+  release();
+  return e == hipSuccess ? ATTN_OK : hip_fail(e, "ring pipeline");
+}
+
 }  // extern "C"

@@ -64,6 +64,9 @@ extern "C" {
 /* Largest sequence length (Nq, Nk) accepted by every entry point. */
 #define ATTN_MAX_SEQ (1 << 28)
 
+/* Most live incoming blocks ring_local_pipelined accepts in one call. */
+#define ATTN_MAX_RING_BLOCKS 4096
+
 /* attn_fwd -- exact attention of q [B,H,Nq,d] against k, v [B,H,Nk,d]; writes o [B,H,Nq,d] and lse [B,H,Nq].
  *   scale       softmax scale applied to q.k (workloads use 1/sqrt(d)); must be finite and > 0.
  *   causal      0 or 1, see "Masks"; q_off, k_off, pos_stride (>= 1) give the global positions.
@@ -175,6 +178,33 @@ int ring_local(const void* q_shard, const attn_kv_block* kv_blocks, int n_blocks
 /* Bytes of workspace ring_local needs: two fp32 (o, lse) buffers of B*H*Nq rows, each 256-byte aligned (the
  * second is used with fp32 inputs only). Returns 0 for negative sizes. */
 size_t ring_local_workspace_bytes(int B, int H, int Nq, int d);
+
+/* ring_local_pipelined -- ring_local with the exchange step of the ring on the same device: compute on the block
+ * in hand while the next one arrives ("架构层解决方案 - Sparse Attention与Ring Attention", Ring Attention /
+ * 计算-通信重叠; "Mosaic多轴注意力分片：突破Transformer长序列处理瓶颈" §3.2). kv_blocks[0] is this device's own
+ * block and is read in place; every later block is an incoming one: it is copied (hipMemcpyAsync on
+ * copy_stream) into one of two receive slots in the workspace while compute_stream attends the block before it,
+ * and merged into the running result in the attention kernel's epilogue (as attn_fwd_merge). Events order the
+ * two streams: a block is attended only once it has landed, and a slot is refilled only once the block in it
+ * has been attended. Incoming blocks may live in any memory hipMemcpyAsync reads (pinned host memory stands in
+ * for the link to the neighbouring device, device memory for a block already received).
+ *   Inputs      bf16 only (in_dtype is ATTN_BF16); blocks that hide every key are neither copied nor attended.
+ *   Streams     compute_stream receives the attention launches and, at the end, holds the result; every copy
+ *               is waited for by a launch on compute_stream, so synchronising compute_stream is enough.
+ *               Both are hipStream_t (NULL = the default stream), both of default priority.
+ *   workspace   at least ring_local_pipelined_workspace_bytes(B, H, Nq, d, Nk_max) bytes (Nk_max = the largest
+ *               incoming block), 256-byte aligned, overlapping nothing else; it must stay untouched until
+ *               compute_stream has passed this call's work. May be NULL only when block 0 is the only live one.
+ *   Errors      as ring_local; ATTN_EINVAL for more than ATTN_MAX_RING_BLOCKS live incoming blocks.
+ *   The result equals ring_local over the same blocks. */
+int ring_local_pipelined(const void* q_shard, const attn_kv_block* kv_blocks, int n_blocks, void* o, float* lse,
+                         int B, int H, int Nq, int d, float scale, int causal, int64_t q_off, int pos_stride,
+                         int o_dtype, void* workspace, size_t workspace_bytes, void* compute_stream,
+                         void* copy_stream);
+
+/* Bytes of workspace ring_local_pipelined needs: the fp32 (o, lse) accumulator of B*H*Nq rows and two receive
+ * slots of bf16 K and V blocks of B*H*Nk_max rows, each buffer 256-byte aligned. Returns 0 for negative sizes. */
+size_t ring_local_pipelined_workspace_bytes(int B, int H, int Nq, int d, int Nk_max);
 
 /* ring_local_plan -- host-only classification of each block, exactly as ring_local decides it (no device
  * work). kinds[i] = 0: every key hidden from every row (skipped); 1: every key visible to every row;

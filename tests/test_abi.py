@@ -296,3 +296,30 @@ def test_attn_fwd_merge_validation(kw, code):
 def test_attn_fwd_merge_zero_sized():
     assert fwd_merge(B=0) == eb.ATTN_OK
     assert fwd_merge(Nq=0, ro=None, rl=None) == eb.ATTN_OK
+
+
+def test_ring_local_pipelined_workspace_and_validation():
+    def a256(x):
+        return (x + 255) // 256 * 256
+    for B, H, Nq, d, nk in [(1, 32, 32768, 128, 32768), (2, 3, 100, 64, 7), (1, 1, 1, 24, 0)]:
+        rows, kv = B * H * Nq, B * H * nk * d * 2
+        assert eb.ring_local_pipelined_workspace_bytes(B, H, Nq, d, nk) == a256(rows * d * 4) + a256(rows * 4) + 4 * a256(kv)
+    assert eb.ring_local_pipelined_workspace_bytes(1, 1, 1, 1, -1) == 0
+    blocks = (eb.KVBlock * 3)(eb.KVBlock(A + B16, A + 2 * B16, 64, 0), eb.KVBlock(A + 3 * B16, A + 4 * B16, 64, 64),
+                              eb.KVBlock(A + 5 * B16, A + 6 * B16, 64, 128))
+    P = dict(q=A, o=A + 7 * B16, lse=A + 8 * B16)
+
+    def call(blocks_, n, ws, ws_bytes, **kw):
+        a = dict(P, B=1, H=2, Nq=64, d=128, scale=0.1, causal=0, q_off=0, stride=1, ot=eb.ATTN_BF16)
+        a.update(kw)
+        return lib.ring_local_pipelined(a["q"], blocks_, n, a["o"], a["lse"], a["B"], a["H"], a["Nq"], a["d"],
+                                        a["scale"], a["causal"], a["q_off"], a["stride"], a["ot"], ws, ws_bytes,
+                                        None, None)
+    assert call(blocks, 3, None, 0) == eb.ATTN_EWORKSPACE                     # two incoming blocks need the slots
+    assert call(blocks, 3, A + 9 * B16, 1024) == eb.ATTN_EWORKSPACE
+    assert call(blocks, 3, A + 9 * B16 + 8, 1 << 24) == eb.ATTN_EINVAL          # misaligned workspace
+    assert call(blocks, 3, A + 7 * B16, 1 << 24) == eb.ATTN_EINVAL              # workspace over o
+    assert call(blocks, -1, None, 0) == eb.ATTN_EINVAL
+    assert call(None, 2, None, 0) == eb.ATTN_EINVAL
+    assert call(blocks, 3, None, 0, d=32) == eb.ATTN_EUNSUPPORTED
+    assert call(blocks, 3, None, 0, B=0) == eb.ATTN_OK
