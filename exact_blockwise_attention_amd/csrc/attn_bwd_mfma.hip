@@ -556,6 +556,10 @@ void attn_bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int xcd_remap) {
   __shared__ __attribute__((aligned(16))) float lb_[kBT];
   __shared__ __attribute__((aligned(16))) float da_[kBT];   // delta of the tile rows
   __shared__ __attribute__((aligned(16))) float db_[kBT];
+  __shared__ __attribute__((aligned(16))) float rla[kBT];   // raw lse and delta as copied, slots a and b
+  __shared__ __attribute__((aligned(16))) float rlb[kBT];
+  __shared__ __attribute__((aligned(16))) float rda[kBT];
+  __shared__ __attribute__((aligned(16))) float rdb[kBT];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -585,25 +589,32 @@ void attn_bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int xcd_remap) {
     copy_tile<D>(Q + bh * a.Nq * D, r0, a.Nq, qd, wave, lane);
     copy_tile<D>(dO + bh * a.Nq * D, r0, a.Nq, od, wave, lane);
   };
-  // wave 0 stages the per-row lse (as the exp2-domain subtrahend) and delta of a stage's 64 rows
-  auto load_rows = [&](int s, float& lv, float& dv) {
+  // The per-row lse and delta of a stage's 64 rows reach LDS in two steps, both by wave 0 and off the critical
+  // path: two stages ahead, a buffer-to-LDS copy of the raw values (issued with the tile copies); one stage ahead,
+  // at the end of a stage, the conversion of lse to the exp2-domain subtrahend (+inf for rows with no visible key
+  // and rows past Nq) into the slot the stage after next reads.
+  auto issue_rows = [&](int s, float* rl, float* rd) {
     const int64_t bh = bh0 + s / nt;
+    const int r0 = (t0 + s % nt) * kBT;
+    const int valid = uniform_clamp(a.Nq - r0, kBT);
+    const __amdgpu_buffer_rsrc_t r1 = make_rsrc(a.lse + bh * a.Nq + r0, (int64_t)valid * 4);
+    const __amdgpu_buffer_rsrc_t r2 = make_rsrc(a.delta + bh * a.Nq + r0, (int64_t)valid * 4);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r1, (lds_void*)rl, 4, (uint32_t)(lane * 4), 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r2, (lds_void*)rd, 4, (uint32_t)(lane * 4), 0, 0, 0);
+  };
+  auto convert_rows = [&](int s, const float* rl, const float* rd, float* lq, float* dq) {
     const int i = (t0 + s % nt) * kBT + lane;
-    lv = INFINITY;
-    dv = 0.0f;
-    if (i < a.Nq) {
-      lv = lse_to_sub(a.lse[bh * a.Nq + i]);
-      dv = a.delta[bh * a.Nq + i];
-    }
+    lq[lane] = i < a.Nq ? lse_to_sub(rl[lane]) : INFINITY;
+    dq[lane] = i < a.Nq ? rd[lane] : 0.0f;
   };
 
   if (nstages > 0) {
     issue_stage(0, qa, oa);
     if (wave == 0) {
-      float lv, dv;
-      load_rows(0, lv, dv);
-      la_[lane] = lv;
-      da_[lane] = dv;
+      issue_rows(0, rla, rda);
+      if (nstages > 1) issue_rows(1, rlb, rdb);
+      wait_vmem_all();
+      convert_rows(0, rla, rda, la_, da_);
     }
   }
 
@@ -633,28 +644,25 @@ void attn_bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int xcd_remap) {
     dv[ct] = f32x16{};
   }
 
+  // stage s: tiles in (qc, oc), converted rows in (lc, dc); the next stage's tiles go to (qn, on) and its rows
+  // are converted from the raw slot (rn_l, rn_d) into (ln, dn); the raw rows of stage s + 2 go to (rs_l, rs_d),
+  // the raw slot stage s used
   auto step = [&](int s, const char* qc, const char* oc, const float* lc, const float* dc, char* qn, char* on,
-                  float* ln, float* dn) {
-    wait_vmem_all();
-    __syncthreads();
-    float lv = 0.0f, dvv = 0.0f;
+                  float* ln, float* dn, const float* rn_l, const float* rn_d, float* rs_l, float* rs_d) {
+    wait_vmem_all();      // this wave's copies of stage s (tiles) and s + 1 (raw rows) have landed
+    __syncthreads();      // every wave's have; every wave is done with stage s - 1
     const bool more = s + 1 < nstages;
-    if (more) {
-      issue_stage(s + 1, qn, on);
-      if (wave == 0) load_rows(s + 1, lv, dvv);
-    }
+    if (more) issue_stage(s + 1, qn, on);
+    if (wave == 0 && s + 2 < nstages) issue_rows(s + 2, rs_l, rs_d);
     const int i0 = (t0 + s % nt) * kBT;
     if (i0 + kBT - 1 >= any_lo && i0 <= any_hi)
       DkdvStage<D>{qc, oc, lc, dc, kf, vf, dk, dv, la, a.scale_log2, !(i0 >= all_lo && i0 + kBT - 1 <= all_hi),
                    vis_lo - i0, vis_hi - i0}();
-    if (more && wave == 0) {
-      ln[lane] = lv;
-      dn[lane] = dvv;
-    }
+    if (more && wave == 0) convert_rows(s + 1, rn_l, rn_d, ln, dn);
   };
   for (int s = 0; s < nstages; s += 2) {
-    step(s, qa, oa, la_, da_, qb, ob, lb_, db_);
-    if (s + 1 < nstages) step(s + 1, qb, ob, lb_, db_, qa, oa, la_, da_);
+    step(s, qa, oa, la_, da_, qb, ob, lb_, db_, rlb, rdb, rla, rda);
+    if (s + 1 < nstages) step(s + 1, qb, ob, lb_, db_, qa, oa, la_, da_, rla, rda, rlb, rdb);
   }
   const int64_t kvrow = kvbh * (int64_t)a.Nk;
   store_grad<D, GF32>(reinterpret_cast<char*>(a.dk) + kvrow * D * (GF32 ? 4 : 2), kw0, a.Nk, lane, dk, a.scale,
