@@ -273,7 +273,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   if (!dtype_ok(in_dtype) || !dtype_ok(o_dtype) || !dtype_ok(grad_dtype)) return fail(ATTN_EINVAL, "unknown dtype code");
   if (in_dtype != ATTN_BF16) return fail(ATTN_EUNSUPPORTED, "the backward takes bf16 q, k, v and dout");
   if (accumulate && grad_dtype != ATTN_F32) return fail(ATTN_EINVAL, "accumulate requires fp32 gradients");
-  if (d != 64 && d != 128) return fail(ATTN_EUNSUPPORTED, "head dim d=%d not supported by the backward (64, 128)", d);
+  if (!head_dim_ok(d)) return fail(ATTN_EUNSUPPORTED, "head dim d=%d not supported by the backward (24, 64, 128)", d);
   const int64_t BH = (int64_t)B * H, BHkv = (int64_t)B * (H > 0 ? Hkv : 0);
   const int64_t qrows = BH * Nq, krows = BHkv * Nk;
   if (qrows == 0 && krows == 0) return ATTN_OK;

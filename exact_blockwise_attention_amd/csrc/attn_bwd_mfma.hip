@@ -49,14 +49,19 @@ constexpr int kWaves = 4;                      // waves per workgroup, 32 owned 
 constexpr int kOwn = 32 * kWaves;              // owned rows per workgroup
 constexpr int32_t kRsrcWord3 = 0x00020000;     // raw buffer, 32-bit data format (gfx9 family)
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr uint32_t kOutOfRange = 0x7ffffff0u;  // a buffer offset past every num_records: the load returns 0
 
+// Geometry of head dim D (24, 64 or 128). D = 24 runs padded to 32: its LDS rows, MFMA k-steps and result tiles
+// have 32 columns, and the padding columns read as zero and are never stored.
 template <int D>
 struct BG {
-  static_assert(D == 64 || D == 128, "head dim 64 or 128");
-  static constexpr int KSTEPS = D / 16;            // MFMA k-steps over the head dim
-  static constexpr int CT = D / 32;                // 32-row tiles of a transposed (d x rows) result
-  static constexpr int RB = D * 2;                 // bytes of one bf16 row
-  static constexpr int CPR = D / 8;                // 16-byte chunks per row
+  static_assert(D == 24 || D == 64 || D == 128, "head dim 24, 64 or 128");
+  static constexpr int DP = (D + 31) / 32 * 32;    // padded head dim
+  static constexpr int KSTEPS = DP / 16;           // MFMA k-steps over the head dim
+  static constexpr int CT = DP / 32;               // 32-row tiles of a transposed (d x rows) result
+  static constexpr int RB = DP * 2;                // bytes of one bf16 row in LDS
+  static constexpr int CPR = DP / 8;               // 16-byte chunks per LDS row
+  static constexpr int CPG = D / 8;                // 16-byte chunks per row in memory (the rest read as zero)
   static constexpr int TILE = kBT * RB;
   static constexpr int INSTR = TILE / 1024;        // wave-wide 16-byte-per-lane copies per tile
   static constexpr int ROWS_PER_INSTR = 1024 / RB;
@@ -68,9 +73,13 @@ struct BG {
 // index of 16 rows that cover row & 15 = 0..15 -> the swizzle must be a bijection of those 16 rows onto distinct
 // bank groups. Transposed reads: 32 lanes read 4 consecutive rows (an aligned group) x 4 chunks of an aligned
 // group of 4 -> the 4 rows must land in 4 different 64-byte quarters of the 256-byte bank row.
+// (Rows of 64 bytes, at D = 24: four rows share a bank row, so row & 3 already picks the quarter and the swizzle
+// only has to separate the four rows of a 16-row group that share a quarter.)
 template <int D>
 __device__ __forceinline__ int swz(int row) {
-  return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+  return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3))
+       : D == 64  ? ((((row >> 1) & 1) << 2) | ((row >> 2) & 3))
+                  : ((row >> 2) & 3);
 }
 // bits 2 and 3 swapped (an involution)
 __device__ __forceinline__ int perm_row(int p) { return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1); }
@@ -116,8 +125,8 @@ __device__ __forceinline__ void copy_tile(const __bf16* X, int r0, int rows_tota
     const int instr = wave * G::PER_WAVE + i;
     const int row = instr * G::ROWS_PER_INSTR + sub;
     const int m = pos ^ swz<D>(row);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(dst + instr * 1024), 16,
-                                             (uint32_t)((row * D + m * 8) * 2), 0, 0, 0);
+    const uint32_t off = m < G::CPG ? (uint32_t)((row * D + m * 8) * 2) : kOutOfRange;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(dst + instr * 1024), 16, off, 0, 0, 0);
   }
 }
 
@@ -174,9 +183,11 @@ __device__ __forceinline__ void load_frags(const __bf16* X, int row0, int rows_t
   const __amdgpu_buffer_rsrc_t r = make_rsrc(X + (int64_t)row0 * D, (int64_t)valid * D * 2);
   const int l32 = lane & 31, hi = lane >> 5;
 #pragma unroll
-  for (int ks = 0; ks < BG<D>::KSTEPS; ++ks)
-    f[ks] = __builtin_bit_cast(bf16x8,
-                               __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)((l32 * D + 16 * ks + 8 * hi) * 2), 0, 0));
+  for (int ks = 0; ks < BG<D>::KSTEPS; ++ks) {
+    const int c = 16 * ks + 8 * hi;
+    const uint32_t off = c < D ? (uint32_t)((l32 * D + c) * 2) : kOutOfRange;
+    f[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  }
 }
 
 // Writes factor * acc for 32 rows (row0 + l%32) of a gradient [rows_total, D] at `out` (fp32 or bf16): register r
@@ -195,6 +206,7 @@ __device__ __forceinline__ void store_grad(void* out, int row0, int rows_total, 
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int c = 32 * ct + 8 * g + 4 * hi;
+      if (c >= D) continue;
       f32x4 y = {acc[ct][4 * g] * factor, acc[ct][4 * g + 1] * factor, acc[ct][4 * g + 2] * factor,
                  acc[ct][4 * g + 3] * factor};
       if constexpr (GF32) {
@@ -281,9 +293,10 @@ void attn_bwd_dq_kernel(BwdArgs a, int n_qtiles, int xcd_remap) {
                                                  (int64_t)valid * D * 4);
 #pragma unroll
       for (int ks = 0; ks < G::KSTEPS; ++ks) {
-        const uint32_t off = (uint32_t)((((lane & 31) * D) + 16 * ks + 8 * hi) * 4);
+        const int c = 16 * ks + 8 * hi;
+        const uint32_t off = c < D ? (uint32_t)((((lane & 31) * D) + c) * 4) : kOutOfRange;
         const f32x4 x0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-        const f32x4 x1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0));
+        const f32x4 x1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, c < D ? off + 16 : off, 0, 0));
         const f32x8 g = __builtin_convertvector(df[ks], f32x8);
 #pragma unroll
         for (int e = 0; e < 4; ++e) dl = __builtin_fmaf(g[e], x0[e], __builtin_fmaf(g[4 + e], x1[e], dl));
@@ -385,9 +398,20 @@ struct DkdvStage {
   static constexpr int NS = 2 * G::KSTEPS;
   static constexpr int NP = 2 * G::CT;
   static constexpr int NT = 2 * NS + 4 * NP;
+  // With few slots (d = 24) elements of one group and the next overlap more: per-element values, bf16 pairs and
+  // row values then get a register each instead of sharing them between groups.
+  static constexpr bool SMALL = NS < 8;
+  static constexpr int ED = SMALL ? 32 : 8;       // per-element arrays, indexed E % ED
+  static constexpr int GD = SMALL ? 4 : 2;        // per-group arrays, indexed kk % GD
   // the slot at which element E (0..31: operand group E/8, element E%8) is formed: groups 0, 1 over slots
   // [NS + 1, 2NS), groups 2, 3 over slots [2NS + 1, 2NS + 2NP)
+  // (d = 24 has too few slots to spread them: each group is formed in one or two slots so that its last step
+  // lands before the first MFMA that takes it)
   static constexpr int elem_slot(int E) {
+    if (NS < 8) {
+      const int kk = E >> 3, e = E & 7;
+      return kk == 0 ? NS + 1 : kk == 1 ? NS + 2 + e / 4 : kk == 2 ? 2 * NS + e / 4 : 2 * NS + 2 + e / 4;
+    }
     return E < 16 ? NS + 1 + (E * (NS - 1)) / 16 : 2 * NS + 1 + ((E - 16) * (2 * NP - 1)) / 16;
   }
 
@@ -406,10 +430,10 @@ struct DkdvStage {
 
   f32x16 s0, s1, p0, p1;
   bf16x8 pb[4], sb[4];
-  float x[8], dd[8], w[8], g[8];  // per element of a group: exponent, dP - delta, weight, score gradient
-  bf16x2 wp[2][4], gp[2][4];      // completed pairs of weights and score gradients (bf16) of groups kk & 1
-  f32x4 lq[2][2], dl[2][2];       // lse (exp2 domain) and delta of groups kk (index kk & 1): the next group's
-                                  // are read while the current group's last elements are still being formed
+  float x[ED], dd[ED], w[ED], g[ED];  // per element: exponent, dP - delta, weight, score gradient
+  bf16x2 wp[GD][4], gp[GD][4];        // completed pairs of weights and score gradients (bf16) per group
+  f32x4 lq[GD][2], dl[GD][2];         // lse (exp2 domain) and delta per group: the next group's are read while
+                                      // the current group's last elements are still being formed
   bf16x8 ring[kLead + 1];
 
   // the A operand of slot I
@@ -429,40 +453,40 @@ struct DkdvStage {
   // eight weights and score gradients after its last element.
   template <int E>
   __device__ __forceinline__ void elem_a() {
-    constexpr int kk = E >> 3, e = E & 7, r = 8 * (kk & 1) + e;
+    constexpr int kk = E >> 3, e = E & 7, r = 8 * (kk & 1) + e, i = E % ED;
     const float sv = (kk >> 1) ? s1[r] : s0[r];
     const float pv = (kk >> 1) ? p1[r] : p0[r];
-    x[e] = __builtin_fmaf(sv, scale_log2, -lq[kk & 1][e >> 2][e & 3]);
-    dd[e] = pv - dl[kk & 1][e >> 2][e & 3];
+    x[i] = __builtin_fmaf(sv, scale_log2, -lq[kk % GD][e >> 2][e & 3]);
+    dd[i] = pv - dl[kk % GD][e >> 2][e & 3];
     // pinned in this slot: the optimiser would otherwise sink the work next to its first use, past the
     // scheduling fences and out of the MFMA shadow it is placed in
-    pin(x[e]);
-    pin(dd[e]);
+    pin(x[i]);
+    pin(dd[i]);
   }
   template <int E>
   __device__ __forceinline__ void elem_b() {
-    constexpr int e = E & 7;
-    w[e] = __builtin_amdgcn_exp2f(x[e]);
-    pin(w[e]);
+    constexpr int i = E % ED;
+    w[i] = __builtin_amdgcn_exp2f(x[i]);
+    pin(w[i]);
   }
   template <int E>
   __device__ __forceinline__ void elem_c() {
-    constexpr int kk = E >> 3, e = E & 7;
-    g[e] = w[e] * dd[e];
+    constexpr int kk = E >> 3, e = E & 7, i = E % ED, ip = (E + ED - 1) % ED;
+    g[i] = w[i] * dd[i];
     if constexpr (e & 1) {
       // each completed pair is rounded to bf16 at once: the next group's elements reuse w and g before this
       // group's last pair is done
-      const f32x2 xw = {w[e - 1], w[e]}, yg = {g[e - 1], g[e]};
-      wp[kk & 1][e >> 1] = __builtin_convertvector(xw, bf16x2);
-      gp[kk & 1][e >> 1] = __builtin_convertvector(yg, bf16x2);
-      pin(wp[kk & 1][e >> 1]);
-      pin(gp[kk & 1][e >> 1]);
+      const f32x2 xw = {w[ip], w[i]}, yg = {g[ip], g[i]};
+      wp[kk % GD][e >> 1] = __builtin_convertvector(xw, bf16x2);
+      gp[kk % GD][e >> 1] = __builtin_convertvector(yg, bf16x2);
+      pin(wp[kk % GD][e >> 1]);
+      pin(gp[kk % GD][e >> 1]);
     } else {
-      pin(g[e]);
+      pin(g[i]);
     }
     if constexpr (e == 7) {
-      const bf16x2(&a)[4] = wp[kk & 1];
-      const bf16x2(&b)[4] = gp[kk & 1];
+      const bf16x2(&a)[4] = wp[kk % GD];
+      const bf16x2(&b)[4] = gp[kk % GD];
       pb[kk] = __builtin_shufflevector(__builtin_shufflevector(a[0], a[1], 0, 1, 2, 3),
                                        __builtin_shufflevector(a[2], a[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
       sb[kk] = __builtin_shufflevector(__builtin_shufflevector(b[0], b[1], 0, 1, 2, 3),
@@ -479,10 +503,10 @@ struct DkdvStage {
   template <int KK>
   __device__ __forceinline__ void read_rows() {
     const int rb = 16 * KK + 8 * la.hi;
-    lq[KK & 1][0] = *reinterpret_cast<const f32x4*>(lc + rb);
-    lq[KK & 1][1] = *reinterpret_cast<const f32x4*>(lc + rb + 4);
-    dl[KK & 1][0] = *reinterpret_cast<const f32x4*>(dc + rb);
-    dl[KK & 1][1] = *reinterpret_cast<const f32x4*>(dc + rb + 4);
+    lq[KK % GD][0] = *reinterpret_cast<const f32x4*>(lc + rb);
+    lq[KK % GD][1] = *reinterpret_cast<const f32x4*>(lc + rb + 4);
+    dl[KK % GD][0] = *reinterpret_cast<const f32x4*>(dc + rb);
+    dl[KK % GD][1] = *reinterpret_cast<const f32x4*>(dc + rb + 4);
   }
 
   __device__ __forceinline__ void mask(f32x16& sm, int off) {
@@ -544,8 +568,12 @@ struct DkdvStage {
 // ------------------------------------------------------------------------------------------------------------
 // dk/dv kernel: 128 keys of one key/value head per workgroup; query tiles of 64 of every query head in its group.
 
+// d = 64 and 128 hold K, V and both accumulators in registers at one wave per SIMD; d = 24 fits two.
+template <int D>
+constexpr int dkdv_waves() { return D >= 64 ? 1 : 2; }
+
 template <int D, bool GF32>
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(dkdv_waves<D>(), dkdv_waves<D>())))
 void attn_bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int xcd_remap) {
   using G = BG<D>;
   __shared__ __attribute__((aligned(1024))) char qa[G::TILE];
@@ -700,6 +728,7 @@ hipError_t launch_attn_bwd_bf16(const BwdArgs& a, int d, int grad_f32, hipStream
   switch (d) {
     case 128: return grad_f32 ? launch_d<128, true>(a, stream) : launch_d<128, false>(a, stream);
     case 64: return grad_f32 ? launch_d<64, true>(a, stream) : launch_d<64, false>(a, stream);
+    case 24: return grad_f32 ? launch_d<24, true>(a, stream) : launch_d<24, false>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -73,8 +73,8 @@ struct BwdArgs {
   int o_f32;          // o is fp32 (else bf16)
   int accumulate;     // add into dq, dk, dv instead of overwriting (fp32 gradients only)
 };
-// bf16 q, k, v, dout on MFMA; d in {64, 128}; gradients fp32 (grad_f32 = 1) or bf16. The dq kernel (which also
-// writes delta) runs first, then the dk/dv kernel, both on `stream`.
+// bf16 q, k, v, dout on MFMA; d in {24, 64, 128} (24 padded to 32); gradients fp32 (grad_f32 = 1) or bf16.
+// The dq kernel (which also writes delta) runs first, then the dk/dv kernel, both on `stream`.
 hipError_t launch_attn_bwd_bf16(const BwdArgs& a, int d, int grad_f32, hipStream_t stream);
 
 struct MergeArgs {

@@ -126,7 +126,7 @@ int attn_fwd_merge(const void* q, const void* k, const void* v, const float* run
  *   dq           [B,H,Nq,d], dk, dv [B,Hkv,Nk,d], in grad_dtype (ATTN_F32 or ATTN_BF16); written.
  *   delta        fp32 [B,H,Nq], written with rowsum(dout * o) (a per-row value the caller may reuse).
  *   accumulate   0: overwrite dq, dk, dv; 1: add into them (ATTN_F32 gradients only).
- *   in_dtype     ATTN_BF16 only (ATTN_EUNSUPPORTED otherwise); d in {64, 128} (ATTN_EUNSUPPORTED otherwise).
+ *   in_dtype     ATTN_BF16 only (ATTN_EUNSUPPORTED otherwise); d in {24, 64, 128} (ATTN_EUNSUPPORTED otherwise).
  *   Masks, offsets, window, scale, stream: as attn_fwd_ex.
  *   Sizes        B, H, Hkv, Nq, Nk >= 0; Nq = 0 writes zero dk, dv (or leaves them, with accumulate); Nk = 0 or
  *                a mask that hides every key writes zero dq; pointers of zero-sized tensors may be NULL.

@@ -241,7 +241,7 @@ def bwd(**kw):
     (dict(stride=0), eb.ATTN_EINVAL),
     (dict(it=eb.ATTN_F32), eb.ATTN_EUNSUPPORTED),           # the backward takes bf16 inputs
     (dict(it=7), eb.ATTN_EINVAL),
-    (dict(d=24), eb.ATTN_EUNSUPPORTED),
+    (dict(d=32), eb.ATTN_EUNSUPPORTED),
     (dict(dq=A + 1), eb.ATTN_EINVAL),                       # misaligned
     (dict(delta=A + 2), eb.ATTN_EINVAL),
     (dict(dq=A + 3 * B16 + 4096), eb.ATTN_EINVAL),          # dq overlaps o

@@ -92,6 +92,9 @@ CASES = [
     (1, 2, 2, 300, 300, 128, True, 0, 0, 1, 1),          # window 1: each row sees only itself
     (1, 2, 2, 129, 1000, 64, False, 0, 0, 1, 0),
     (1, 2, 2, 1000, 65, 128, True, 5, 0, 1, 0),
+    (1, 3, 3, 333, 333, 24, True, 0, 0, 1, 0),           # d = 24 (padded to 32), as the tabular row axis
+    (2, 4, 2, 150, 260, 24, False, 0, 0, 1, 0),
+    (1, 4, 1, 200, 200, 24, True, 0, 0, 1, 37),
 ]
 
 
