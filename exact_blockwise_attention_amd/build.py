@@ -23,7 +23,7 @@ LIB = os.path.join(PKG, "libebattn.so")
 ARCH = os.environ.get("EBATTN_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["api.hip", "attn_fwd_mfma.hip", "attn_fwd_f32.hip", "attn_fwd_short.hip", "attn_bwd_mfma.hip",
-           "lse_merge.hip"]
+           "attn_bwd_f32.hip", "lse_merge.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -271,7 +271,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   if (window < 0 || window > kOffLimit) return fail(ATTN_EINVAL, "window out of range (got %lld)", (long long)window);
   if (window > 0 && !causal) return fail(ATTN_EINVAL, "a sliding window requires causal = 1");
   if (!dtype_ok(in_dtype) || !dtype_ok(o_dtype) || !dtype_ok(grad_dtype)) return fail(ATTN_EINVAL, "unknown dtype code");
-  if (in_dtype != ATTN_BF16) return fail(ATTN_EUNSUPPORTED, "the backward takes bf16 q, k, v and dout");
+  if (in_dtype == ATTN_F32 && o_dtype != ATTN_F32) return fail(ATTN_EINVAL, "fp32 inputs come with an fp32 o");
   if (accumulate && grad_dtype != ATTN_F32) return fail(ATTN_EINVAL, "accumulate requires fp32 gradients");
   if (!head_dim_ok(d)) return fail(ATTN_EUNSUPPORTED, "head dim d=%d not supported by the backward (24, 64, 128)", d);
   const int64_t BH = (int64_t)B * H, BHkv = (int64_t)B * (H > 0 ? Hkv : 0);
@@ -289,11 +289,11 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
       return fail(ATTN_EINVAL, "k, v, dk and dv must be 16-byte aligned");
   }
   // the four outputs must not overlap each other or any input
-  const int64_t gb = elem_bytes(grad_dtype);
+  const int64_t gb = elem_bytes(grad_dtype), ib = elem_bytes(in_dtype);
   const Span outs[4] = {span(dq, qrows * d * gb), span(dk, krows * d * gb), span(dv, krows * d * gb),
                         span(delta, qrows * 4)};
-  const Span ins[6] = {span(q, qrows * d * 2), span(k, krows * d * 2), span(v, krows * d * 2),
-                       span(o, qrows * d * elem_bytes(o_dtype)), span(lse, qrows * 4), span(dout, qrows * d * 2)};
+  const Span ins[6] = {span(q, qrows * d * ib), span(k, krows * d * ib), span(v, krows * d * ib),
+                       span(o, qrows * d * elem_bytes(o_dtype)), span(lse, qrows * 4), span(dout, qrows * d * ib)};
   for (int i = 0; i < 4; ++i) {
     for (int j = i + 1; j < 4; ++j)
       if (overlap(outs[i], outs[j])) return fail(ATTN_EINVAL, "dq, dk, dv and delta must not overlap");
@@ -326,7 +326,9 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   a.o_f32 = o_dtype == ATTN_F32;
   a.accumulate = accumulate;
   (void)hipGetLastError();  // drop a stale error so a failure below is attributed to this call
-  const hipError_t e = ebattn::launch_attn_bwd_bf16(a, d, grad_dtype == ATTN_F32, reinterpret_cast<hipStream_t>(stream));
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const hipError_t e = in_dtype == ATTN_F32 ? ebattn::launch_attn_bwd_f32(a, d, grad_dtype == ATTN_F32, st)
+                                            : ebattn::launch_attn_bwd_bf16(a, d, grad_dtype == ATTN_F32, st);
   return e == hipSuccess ? ATTN_OK : hip_fail(e, "backward launch");
 }
 

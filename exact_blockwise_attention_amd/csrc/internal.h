@@ -76,6 +76,9 @@ struct BwdArgs {
 // bf16 q, k, v, dout on MFMA; d in {24, 64, 128} (24 padded to 32); gradients fp32 (grad_f32 = 1) or bf16.
 // The dq kernel (which also writes delta) runs first, then the dk/dv kernel, both on `stream`.
 hipError_t launch_attn_bwd_bf16(const BwdArgs& a, int d, int grad_f32, hipStream_t stream);
+// fp32 q, k, v, dout and o on the vector ALU (the fp32 correctness path); d in {24, 64, 128}; same order of
+// kernels and same outputs as the bf16 path.
+hipError_t launch_attn_bwd_f32(const BwdArgs& a, int d, int grad_f32, hipStream_t stream);
 
 struct MergeArgs {
   const void* o_a;

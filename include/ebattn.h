@@ -121,18 +121,19 @@ int attn_fwd_merge(const void* q, const void* k, const void* v, const float* run
  * forward when lse and o are the forward's results over the same keys. When k, v are one block of a larger key
  * set (a ring share), pass the lse and o of the FULL key set: the returned dq is then that block's contribution
  * (dq over the full set is the sum over the blocks; see `accumulate`), and dk, dv are exact for the block's keys.
- *   q, dout      bf16 [B,H,Nq,d]; k, v bf16 [B,Hkv,Nk,d] (Hkv divides H, as attn_fwd_ex).
+ *   q, dout      [B,H,Nq,d]; k, v [B,Hkv,Nk,d] (Hkv divides H, as attn_fwd_ex), all in in_dtype.
  *   o            [B,H,Nq,d] in o_dtype (ATTN_BF16 or ATTN_F32); lse fp32 [B,H,Nq] (-inf rows contribute nothing).
  *   dq           [B,H,Nq,d], dk, dv [B,Hkv,Nk,d], in grad_dtype (ATTN_F32 or ATTN_BF16); written.
  *   delta        fp32 [B,H,Nq], written with rowsum(dout * o) (a per-row value the caller may reuse).
  *   accumulate   0: overwrite dq, dk, dv; 1: add into them (ATTN_F32 gradients only).
- *   in_dtype     ATTN_BF16 only (ATTN_EUNSUPPORTED otherwise); d in {24, 64, 128} (ATTN_EUNSUPPORTED otherwise).
+ *   in_dtype     ATTN_BF16 (MFMA) or ATTN_F32 (vector ALU, the fp32 correctness path; o must then be ATTN_F32 and
+ *                q, k, v, dout fp32); d in {24, 64, 128} (ATTN_EUNSUPPORTED otherwise).
  *   Masks, offsets, window, scale, stream: as attn_fwd_ex.
  *   Sizes        B, H, Hkv, Nq, Nk >= 0; Nq = 0 writes zero dk, dv (or leaves them, with accumulate); Nk = 0 or
  *                a mask that hides every key writes zero dq; pointers of zero-sized tensors may be NULL.
  *   Overlap      dq, dk, dv and delta must not overlap each other or any input (ATTN_EINVAL).
- *   Numerics     bf16 MFMA products with fp32 accumulation: P is rounded to bf16 for dv and ds to bf16 for dq
- *                and dk; lse, delta and the exponentials are fp32.
+ *   Numerics     bf16 inputs: bf16 MFMA products with fp32 accumulation, P rounded to bf16 for dv and ds to
+ *                bf16 for dq and dk; fp32 inputs: fp32 throughout. lse, delta and the exponentials are fp32.
  *   Two kernels run in order on `stream`: dq (which also writes delta), then dk and dv. */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
              void* dq, void* dk, void* dv, float* delta,

@@ -239,7 +239,7 @@ def bwd(**kw):
     (dict(window=8, causal=0), eb.ATTN_EINVAL),
     (dict(scale=0.0), eb.ATTN_EINVAL),
     (dict(stride=0), eb.ATTN_EINVAL),
-    (dict(it=eb.ATTN_F32), eb.ATTN_EUNSUPPORTED),           # the backward takes bf16 inputs
+    (dict(it=eb.ATTN_F32), eb.ATTN_EINVAL),                 # fp32 inputs need an fp32 o
     (dict(it=7), eb.ATTN_EINVAL),
     (dict(d=32), eb.ATTN_EUNSUPPORTED),
     (dict(dq=A + 1), eb.ATTN_EINVAL),                       # misaligned

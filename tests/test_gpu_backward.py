@@ -18,8 +18,8 @@ import numpy as np
 import pytest
 
 import oracle
-from tests.gpu_util import dev_bf16, host_f64, torch
-from workloads import bf16_bits_to_f64, normal_bf16_bits
+from tests.gpu_util import dev_bf16, dev_f32, host_f64, torch
+from workloads import bf16_bits_to_f64, normal_bf16_bits, normal_f32
 
 pytestmark = pytest.mark.gpu
 
@@ -38,7 +38,7 @@ def _inputs(seed, B, H, Hkv, Nq, Nk, d):
             normal_bf16_bits(seed, "v", (B, Hkv, Nk, d)), normal_bf16_bits(seed, "do", (B, H, Nq, d)))
 
 
-def compare_grad(got, ref, what):
+def compare_grad(got, ref, what, tol_norm=None, tol_max=None):
     got = np.asarray(got, dtype=np.float64)
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
     assert np.isfinite(got).all(), f"{what}: non-finite values"
@@ -50,8 +50,10 @@ def compare_grad(got, ref, what):
     if nref == 0:
         assert err_max <= 1e-5, f"{what}: expected zeros up to fp32 rounding, got {err_max}"
         return
-    assert err_norm <= TOL_NORM, f"{what}: normwise error {err_norm}"
-    assert err_max <= TOL_MAX * scale, f"{what}: max error {err_max} > {TOL_MAX} * {scale}"
+    tol_norm = TOL_NORM if tol_norm is None else tol_norm
+    tol_max = TOL_MAX if tol_max is None else tol_max
+    assert err_norm <= tol_norm, f"{what}: normwise error {err_norm}"
+    assert err_max <= tol_max * scale, f"{what}: max error {err_max} > {tol_max} * {scale}"
 
 
 def run_case(eb, case, seed=31, o_f32=False, grad="f32"):
@@ -212,3 +214,37 @@ def test_backward_causal_8k_full_size_heads(eb):
         ref = oracle.attention_backward(*(bf16_bits_to_f64(x[sl]) for x in (Q, K, V, dO)), c.scale, causal=True)
         for name, g, r in zip(("dq", "dk", "dv", "delta"), (dq, dk, dv, delta), ref):
             compare_grad(host_f64(g[sl]), r, f"causal_8k b{b} h{h} {name}")
+
+
+# fp32 inputs (the vector-ALU path): fp32 arithmetic throughout, so the bar is 1e-5 normwise and 1e-4 of the
+# tensor's largest magnitude elementwise (sums of up to a thousand fp32 products of O(1) terms)
+F32_CASES = [
+    (1, 2, 2, 150, 170, 128, True, 0, 0, 1, 0),
+    (1, 4, 2, 100, 90, 64, False, 0, 0, 1, 0),
+    (2, 3, 3, 77, 77, 24, True, 0, 0, 1, 20),
+    (1, 2, 1, 100, 200, 64, True, 100, 0, 1, 0),
+    (1, 2, 2, 60, 60, 128, True, 1, 3, 4, 0),        # striped: row 0 sees nothing
+]
+
+
+@pytest.mark.parametrize("case", F32_CASES, ids=lambda c: "B{}H{}kv{}q{}k{}d{}c{}qo{}ko{}s{}w{}".format(*c))
+@pytest.mark.parametrize("grad", ["f32", "bf16"])
+def test_backward_fp32_inputs(eb, case, grad):
+    t = torch()
+    B, H, Hkv, Nq, Nk, d, causal, q_off, k_off, stride, window = case
+    q, k, v, do = (normal_f32(37, n, (B, hh, N, d)) for n, hh, N in
+                   (("q", H, Nq), ("k", Hkv, Nk), ("v", Hkv, Nk), ("do", H, Nq)))
+    scale = 1 / math.sqrt(d)
+    mask = dict(causal=causal, q_off=q_off, k_off=k_off, pos_stride=stride, window=window)
+    print(f"[case] backward fp32 {case} grad={grad}", flush=True)
+    qd, kd, vd, dod = dev_f32(q), dev_f32(k), dev_f32(v), dev_f32(do)
+    o, lse = eb.attn_fwd_ex(qd, kd, vd, scale=scale, **mask)
+    dq, dk, dv, delta = eb.attn_bwd(qd, kd, vd, o, lse, dod, scale=scale,
+                                    grad_dtype=t.float32 if grad == "f32" else t.bfloat16, **mask)
+    t.cuda.synchronize()
+    ref = oracle.attention_backward(q, k, v, do, scale, causal=causal, q_off=q_off, k_off=k_off, stride=stride,
+                                    window=window)
+    tn, tm = (1e-5, 1e-4) if grad == "f32" else (TOL_NORM, TOL_MAX)
+    for name, g, r in zip(("dq", "dk", "dv", "delta"), (dq, dk, dv, delta), ref):
+        compare_grad(host_f64(g), r, f"fp32 {case} {name}", tn if name != "delta" else 1e-5,
+                     tm if name != "delta" else 1e-4)
