@@ -13,7 +13,8 @@ seeded and already resident in HBM. The printed JSON line reports:
   cpu_baseline  the float64 oracle timed on this host on a bounded row sample of the same workload;
   extra      secondary measurements: the LSE merge at the ring-share shape (HBM-bound), the ring-share /
              striped workloads end to end, both axes of the tabular workload, a sliding-window
-             grouped-query shape (attn_fwd_ex), and the backward (attn_bwd) on the forward's workload.
+             grouped-query shape (attn_fwd_ex), single-call causal attention at N = 32768 and 131072, and the
+             backward (attn_bwd) on the forward's workload.
 """
 from __future__ import annotations
 
@@ -181,6 +182,8 @@ def bench_extra(torch, eb, dev, steps):
     torch.cuda.empty_cache()
     out.update(bench_window_gqa(torch, eb, dev, steps))
     torch.cuda.empty_cache()
+    out.update(bench_long(torch, eb, dev, steps))
+    torch.cuda.empty_cache()
     out.update(bench_backward(torch, eb, dev, steps))
     return out
 
@@ -213,6 +216,26 @@ def bench_ring_pipeline(torch, eb, dev, c3, qd, kd, vd, order, ms_compute, fl, s
     return {"ms": ms_pipe, "TFLOP/s": fl / ms_pipe / 1e9, "ms_compute_only": ms_compute, "ms_copies_only": ms_copy,
             "copy_GB/s": nbytes / ms_copy / 1e6, "bytes_copied": nbytes,
             "hidden_fraction_of_copies": (ms_compute + ms_copy - ms_pipe) / ms_copy}
+
+
+def bench_long(torch, eb, dev, steps):
+    """Single-call causal self-attention at the long end of the 8K..128K range: B=1, H=32, d=128, N = 32768 and
+    131072 (the whole sequence on one GPU, no ring)."""
+    from workloads import CONFIGS, normal_bf16_bits
+    from workloads import accounting as acc
+    out = {}
+    for key in ("causal_32k", "causal_128k"):
+        c = CONFIGS[key]
+        q, k, v = (upload_bf16(normal_bf16_bits(c.seed, t, (c.B, c.H, c.Nq, c.d)), torch, dev) for t in "qkv")
+        o = torch.empty_like(q)
+        lse = torch.empty((c.B, c.H, c.Nq), dtype=torch.float32, device=dev)
+        ms = time_region(torch, lambda: eb.attn_fwd(q, k, v, scale=c.scale, causal=True, out=o, lse=lse),
+                         max(2, steps // 4) if c.Nq > 40000 else max(steps, 10), 1)
+        fl = acc.attention_flops(acc.config_pairs(c), c.d)
+        out[key] = {"ms": ms, "TFLOP/s": fl / ms / 1e9, "frac_mfma_peak": fl / ms / 1e9 / PEAK_BF16_TFLOPS}
+        del q, k, v, o, lse
+        torch.cuda.empty_cache()
+    return out
 
 
 def bench_window_gqa(torch, eb, dev, steps):

@@ -229,3 +229,22 @@ def test_tabular_row_and_feature_axes(eb):
     o_ref, l_ref = oracle.attention(bf16_bits_to_f64(Qf[sel]), bf16_bits_to_f64(Kf[sel]), bf16_bits_to_f64(Vf[sel]),
                                     cr.scale)
     compare(oh[sel], lh[sel], o_ref, l_ref, TOL_BF16, 1e-5, what="tabular features")
+
+
+@pytest.mark.parametrize("key", ["causal_32k", "causal_128k"])
+def test_causal_long_single_call_sampled(eb, key):
+    """The long single-call workloads the bench times (B=1, H=32, d=128, causal, N = 32768 and 131072): sampled
+    rows of three heads against the oracle."""
+    t = torch()
+    c = CONFIGS[key]
+    print(f"[case] {key}: generating Q/K/V (N={c.Nq}, H={c.H})", flush=True)
+    Q, K, V = (normal_bf16_bits(c.seed, n, (c.B, c.H, c.Nq, c.d)) for n in "qkv")
+    o, lse = eb.attn_fwd(dev_bf16(Q), dev_bf16(K), dev_bf16(V), scale=c.scale, causal=True)
+    t.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    heads = [(0, 0), (0, 17), (0, 31)]
+    rows = sample_rows(c.Nq, 128, 96, rng)
+    o_ref, l_ref = _oracle_rows(Q, K, V, heads, rows, c.scale, causal=True)
+    oh, lh = host_f64(o), host_f64(lse)
+    compare(np.stack([oh[b, h, rows] for b, h in heads]), np.stack([lh[b, h, rows] for b, h in heads]), o_ref, l_ref,
+            TOL_BF16, TOL_LSE, what=f"{key} single call")

@@ -48,6 +48,11 @@ def _causal_8k() -> Config:
                   blocks=((8192, 0),), global_N=8192)
 
 
+def _causal_long(n: int, key: str) -> Config:
+    return Config(key, 6, f"causal self-attention bf16 on one GPU, B=1 H=32 N={n} d=128",
+                  B=1, H=32, Nq=n, d=128, dtype="bf16", causal=True, blocks=((n, 0),), global_N=n)
+
+
 def _ring_rank2of4() -> Config:
     n = 32768
     return Config("ring_rank2of4_128k", 3,
@@ -81,6 +86,8 @@ def _tabular_features() -> Config:
 CONFIGS = {
     "tiny_f32": _tiny_f32(),
     "causal_8k": _causal_8k(),
+    "causal_32k": _causal_long(32768, "causal_32k"),
+    "causal_128k": _causal_long(131072, "causal_128k"),
     "ring_rank2of4_128k": _ring_rank2of4(),
     "striped_r0_64k": striped(0),
     "striped_r1_64k": striped(1),
