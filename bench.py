@@ -11,7 +11,8 @@ seeded and already resident in HBM. The printed JSON line reports:
              launch from the committed rocprofv3 counter summary when it was taken on the current kernel
              source, else null;
   cpu_baseline  the float64 oracle timed on this host on a bounded row sample of the same workload;
-  extra      secondary measurements: the LSE merge at the ring-share shape (HBM-bound), the ring-share /
+  extra      secondary measurements: the LSE merge at the ring-share shape (HBM-bound) and at other sizes and
+             dtypes, the ring share's attention per block, the ring-share /
              striped workloads end to end, both axes of the tabular workload, a sliding-window
              grouped-query shape (attn_fwd_ex), single-call causal attention at N = 32768 and 131072, and the
              backward (attn_bwd) on the forward's workload.
@@ -125,11 +126,44 @@ def bench_merge(torch, eb, dev, steps):
             "bytes_per_launch": nbytes}
 
 
+def bench_merge_sweep(torch, eb, dev, steps):
+    """The merge at other sizes and dtypes: the striped share's rows (16*16384 x 128, fp32 in place, 406 MB), a
+    point above 4 GB (4*1048576 rows x 128, fp32 in place, 6.5 GB), and the ring-share rows with a bf16 output
+    (fp32 partials) and with bf16 partials and output."""
+    from workloads import accounting as acc
+    out = {}
+    g = torch.Generator(device=dev)
+    g.manual_seed(4)
+    for name, rows, pt, ot in (("f32_inplace_262144_rows", 16 * 16384, torch.float32, torch.float32),
+                               ("f32_inplace_4M_rows", 4 * 1048576, torch.float32, torch.float32),
+                               ("f32_to_bf16_1M_rows", 1048576, torch.float32, torch.bfloat16),
+                               ("bf16_to_bf16_1M_rows", 1048576, torch.bfloat16, torch.bfloat16)):
+        d = 128
+        oa = torch.randn((rows, d), device=dev, generator=g).to(pt)
+        ob = torch.randn((rows, d), device=dev, generator=g).to(pt)
+        la = torch.randn((rows,), device=dev, generator=g)
+        lb = torch.randn((rows,), device=dev, generator=g)
+        if ot == pt:
+            fn = lambda: eb.attn_lse_merge(oa, la, ob, lb, out=oa, lse_out=la)   # noqa: E731
+        else:
+            o = torch.empty((rows, d), device=dev, dtype=ot)
+            lo = torch.empty((rows,), device=dev)
+            fn = lambda: eb.attn_lse_merge(oa, la, ob, lb, out=o, lse_out=lo)    # noqa: E731
+        ms = time_region(torch, fn, max(steps, 10), 3)
+        nbytes = acc.merge_bytes(rows, d, oa.element_size(), 2 if ot == torch.bfloat16 else 4)
+        out[name] = {"ms": ms, "GB/s": nbytes / ms / 1e6, "frac_hbm_peak": nbytes / ms / 1e6 / PEAK_HBM_GBS,
+                     "bytes_per_launch": nbytes}
+        del oa, ob, la, lb
+        torch.cuda.empty_cache()
+    return out
+
+
 def bench_extra(torch, eb, dev, steps):
     """Merge bandwidth at the ring-share shape, and the ring-share / striped workloads end to end."""
     from workloads import CONFIGS, normal_bf16_bits
     from workloads import accounting as acc
     out = {"lse_merge_f32_inplace_1M_rows_d128": bench_merge(torch, eb, dev, steps)}
+    out["lse_merge_sweep_d128"] = bench_merge_sweep(torch, eb, dev, steps)
     # ring share, rank 2 of 4, global N = 131072
     c3 = CONFIGS["ring_rank2of4_128k"]
     n = c3.Nq
@@ -154,6 +188,20 @@ def bench_extra(torch, eb, dev, steps):
     fl = acc.attention_flops(acc.config_pairs(c3), c3.d)
     out["ring_local_rank2of4_128k"] = {"ms": ms, "TFLOP/s": fl / ms / 1e9, "frac_mfma_peak": fl / ms / 1e9 / PEAK_BF16_TFLOPS}
     out["ring_pipelined_rank2of4_128k_h2d"] = bench_ring_pipeline(torch, eb, dev, c3, qd, kd, vd, order, ms, fl, steps)
+    # the same share's attention alone, one live block at a time (fp32 partial output, no merge)
+    per_block = {}
+    po = torch.empty(qd.shape, dtype=torch.float32, device=dev)
+    pl = torch.empty((c3.B, c3.H, n), dtype=torch.float32, device=dev)
+    for s_ in order:
+        pairs = c3.B * c3.H * acc.visible_pairs(n, n, True, c3.q_off, s_ * n)
+        if pairs == 0:
+            continue
+        ms_b = time_region(torch, lambda: eb.attn_fwd(qd, kd[s_], vd[s_], causal=True, q_off=c3.q_off, k_off=s_ * n,
+                                                      out=po, lse=pl), max(2, steps // 4), 1)
+        fb = acc.attention_flops(pairs, c3.d)
+        per_block[f"block{s_}"] = {"ms": ms_b, "TFLOP/s": fb / ms_b / 1e9, "frac_mfma_peak": fb / ms_b / 1e9 / PEAK_BF16_TFLOPS}
+    out["ring_rank2of4_128k_attn_fwd_per_block"] = per_block
+    del po, pl
     del qd, kd, vd, blocks, ws, o, lse
     torch.cuda.empty_cache()
     # striped: all four query stripes of N = 65536, H = 16
