@@ -422,7 +422,8 @@ def ring_local_pipelined(q_shard, kv_blocks, *, scale: Optional[float] = None, c
     arr, n = _blocks(kv_blocks)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(lib.ring_local_pipelined(_ptr(q_shard), arr, n, _ptr(out), _ptr(lse), B, H, Nq, d, scale, int(causal),
-                                    int(q_off), int(pos_stride), _code(out.dtype), _ptr(workspace), ws_bytes,
-                                    _stream(q_shard), copy_stream.cuda_stream))
+    with torch.cuda.device(q_shard.device):   # the call creates its events on the current device
+        _check(lib.ring_local_pipelined(_ptr(q_shard), arr, n, _ptr(out), _ptr(lse), B, H, Nq, d, scale,
+                                        int(causal), int(q_off), int(pos_stride), _code(out.dtype), _ptr(workspace),
+                                        ws_bytes, _stream(q_shard), copy_stream.cuda_stream))
     return out, lse

@@ -192,7 +192,8 @@ size_t ring_local_workspace_bytes(int B, int H, int Nq, int d);
  *   Inputs      bf16 only (in_dtype is ATTN_BF16); blocks that hide every key are neither copied nor attended.
  *   Streams     compute_stream receives the attention launches and, at the end, holds the result; every copy
  *               is waited for by a launch on compute_stream, so synchronising compute_stream is enough.
- *               Both are hipStream_t (NULL = the default stream), both of default priority.
+ *               Both are hipStream_t (NULL = the default stream), both of default priority, both on the
+ *               current device (the call creates its ordering events there).
  *   workspace   at least ring_local_pipelined_workspace_bytes(B, H, Nq, d, Nk_max) bytes (Nk_max = the largest
  *               incoming block), 256-byte aligned, overlapping nothing else; it must stay untouched until
  *               compute_stream has passed this call's work. May be NULL only when block 0 is the only live one.
