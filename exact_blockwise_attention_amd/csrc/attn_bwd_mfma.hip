@@ -24,6 +24,7 @@
 // (ds_read_b64_tr_b16, contraction over the rows); one XOR swizzle of the 16-byte chunks of a row keeps both
 // patterns free of bank conflicts on the 64 four-byte banks. Tiles are copied HBM -> LDS by the buffer unit
 // (buffer_load ... lds), double-buffered, one barrier per tile.
+#include <type_traits>
 #include <utility>
 
 #include "internal.h"
@@ -379,18 +380,25 @@ void attn_bwd_dq_kernel(BwdArgs a, int n_qtiles, int xcd_remap) {
 }
 
 // ------------------------------------------------------------------------------------------------------------
-// One query tile of the dk/dv kernel for one wave, laid out slot by slot: one MFMA per slot, the LDS operand
-// reads kLead slots ahead, and a scheduling fence after every slot so that the compiler keeps the order (one wave
-// per SIMD: nothing else hides the LDS latency or the vector-ALU work). With NS = 2*KSTEPS and NP = 2*CT:
+// The dk/dv stages below are laid out slot by slot: one MFMA per slot, the LDS operand reads kLead slots ahead,
+// and a scheduling fence after every slot so that the compiler keeps the order (with few waves per SIMD nothing
+// else hides the LDS latency or the vector-ALU work). Register r of the score and dP accumulators s_h / p_h
+// (h = 0: tile rows 0..31, h = 1: rows 32..63) holds tile row 32*h + 16*(r/8) + 8*hi + r%8: operand group
+// kk = 2*h + r/8 and element r%8 of the lane's 8 rows 16*kk + 8*hi .. +7 (whose lse and delta are read from LDS
+// as two float4 each).
+constexpr int kLead = 3;
+
+// One query tile of the dk/dv kernel for one wave at d = 24 (padded to 32), in one stage. With NS = 2*KSTEPS and
+// NP = 2*CT:
 //   slots [0, NS)           S and dP of tile rows 0..31 (accumulators s0, p0)
 //   slots [NS, 2NS)         S and dP of rows 32..63 (s1, p1), beside the weights and score gradients of rows
-//                           0..31 (operand groups kk = 0, 1: rows 16*kk .. +15)
+//                           0..31 (operand groups kk = 0, 1)
 //   slots [2NS, 2NS + 2NP)  dV += dO^T P and dK += Q^T dS for kk = 0, 1, beside the weights and score gradients
 //                           of rows 32..63 (kk = 2, 3)
 //   slots [2NS + 2NP, ...)  dV and dK for kk = 2, 3.
-// Register r of s_h / p_h holds tile row 32*h + 16*(r/8) + 8*hi + r%8: operand group kk = 2*h + r/8 and element
-// r%8 of the lane's 8 rows 16*kk + 8*hi .. +7 (whose lse and delta are read from LDS as two float4 each).
-constexpr int kLead = 3;
+// The stage is too short to spread the element steps: each operand group is formed in one or two slots, so that
+// its last step lands before the first MFMA that takes it, and every element, bf16 pair and group row value has
+// a register of its own.
 
 template <int D>
 struct DkdvStage {
@@ -398,21 +406,13 @@ struct DkdvStage {
   static constexpr int NS = 2 * G::KSTEPS;
   static constexpr int NP = 2 * G::CT;
   static constexpr int NT = 2 * NS + 4 * NP;
-  // With few slots (d = 24) elements of one group and the next overlap more: per-element values, bf16 pairs and
-  // row values then get a register each instead of sharing them between groups.
-  static constexpr bool SMALL = NS < 8;
-  static constexpr int ED = SMALL ? 32 : 8;       // per-element arrays, indexed E % ED
-  static constexpr int GD = SMALL ? 4 : 2;        // per-group arrays, indexed kk % GD
-  // the slot at which element E (0..31: operand group E/8, element E%8) is formed: groups 0, 1 over slots
-  // [NS + 1, 2NS), groups 2, 3 over slots [2NS + 1, 2NS + 2NP)
-  // (d = 24 has too few slots to spread them: each group is formed in one or two slots so that its last step
-  // lands before the first MFMA that takes it)
+  static_assert(NS < 8, "d = 64 and 128 take the pipelined stage");
+  static constexpr int ED = 32;                   // per-element arrays, indexed E % ED
+  static constexpr int GD = 4;                    // per-group arrays, indexed kk % GD
+  // the slot at which element E (0..31: operand group E/8, element E%8) is formed
   static constexpr int elem_slot(int E) {
-    if (NS < 8) {
-      const int kk = E >> 3, e = E & 7;
-      return kk == 0 ? NS + 1 : kk == 1 ? NS + 2 + e / 4 : kk == 2 ? 2 * NS + e / 4 : 2 * NS + 2 + e / 4;
-    }
-    return E < 16 ? NS + 1 + (E * (NS - 1)) / 16 : 2 * NS + 1 + ((E - 16) * (2 * NP - 1)) / 16;
+    const int kk = E >> 3, e = E & 7;
+    return kk == 0 ? NS + 1 : kk == 1 ? NS + 2 + e / 4 : kk == 2 ? 2 * NS + e / 4 : 2 * NS + 2 + e / 4;
   }
 
   const char* qc;
@@ -566,6 +566,180 @@ struct DkdvStage {
 };
 
 // ------------------------------------------------------------------------------------------------------------
+// The dk/dv stage for d = 64 and 128, pipelined across stages so that every phase of 2*KSTEPS MFMAs carries one
+// operand group's weights and score gradients (eight elements per lane) beside it. With PH = 2*KSTEPS slots per
+// phase, stage s runs
+//   phase 0: S, dP of rows 0..31 of stage s        beside group 3 (rows 48..63) of stage s - 1
+//   phase 1: dV, dK for groups 2, 3 of stage s - 1  beside group 0 (rows 0..15) of stage s
+//   phase 2: S, dP of rows 32..63 of stage s       beside group 1 (rows 16..31)
+//   phase 3: dV, dK for groups 0, 1 of stage s      beside group 2 (rows 32..47)
+// so a stage reads the Q and dO tiles of the stage before it too (three tile buffers), and the first stage and
+// a final drain half-stage leave out the parts that have no stage before or after them.
+template <int D>
+struct DkdvPipe {
+  using G = BG<D>;
+  static constexpr int PH = 2 * G::KSTEPS;        // slots per phase: the MFMAs of one S/dP half
+  static constexpr int NP = 2 * G::CT;            // MFMAs of one group's dV/dK
+  static_assert(PH == 2 * NP && PH >= 8, "the phase plan needs d = 64 or 128");
+  static constexpr int T = 4 * PH;
+  // a-step slot of element e of group g (g = 3: the previous stage's last group, in phase 0)
+  static constexpr int elem_slot(int g, int e) { return (g == 3 ? 0 : g + 1) * PH + 1 + (e * (PH - 3)) / 8; }
+  // lse and delta of group g: three slots before its first element (group 3's at the end of its own stage)
+  static constexpr int read_slot(int g) { return g == 3 ? T - 2 : elem_slot(g, 0) - 3; }
+
+  const bf16x8 (&kf)[G::KSTEPS];
+  const bf16x8 (&vf)[G::KSTEPS];
+  f32x16 (&dk)[G::CT];
+  f32x16 (&dv)[G::CT];
+  const Lanes<D>& la;
+  float scale_log2;
+
+  // carried from one stage to the next: the second S/dP half (its last group is formed in the next stage) and the
+  // bf16 operands of groups 2 and 3 (their dV/dK MFMAs run in the next stage)
+  f32x16 s0, s1, p0, p1;
+  bf16x8 pb[4], sb[4];
+  float x[8], dd[8], w[8], g[8];
+  bf16x2 wp[2][4], gp[2][4];
+  f32x4 lq[2][2], dl[2][2];
+  bf16x8 ring[kLead + 1];
+  // this stage's and the previous stage's tiles, this stage's rows and mask
+  const char *qc, *oc, *qp, *op;
+  const float *lc, *dc;
+  bool masked;
+  int lo, up;
+
+  template <bool PREV, bool CUR>
+  static constexpr bool has_mfma(int I) { return (I / PH == 1) ? PREV : CUR; }
+
+  template <bool PREV, bool CUR, int I>
+  __device__ __forceinline__ bf16x8 frag() const {
+    constexpr int ph = I / PH, j = I % PH;
+    if constexpr (ph == 0 || ph == 2) {
+      return row_frag<D>((j & 1) ? oc : qc, la, ph / 2, j >> 1);
+    } else if constexpr (ph == 1) {
+      constexpr int jj = j % NP;
+      return tr_frag<D>((jj & 1) ? qp : op, la, 2 + j / NP, jj >> 1);
+    } else {
+      constexpr int jj = j % NP;
+      return tr_frag<D>((jj & 1) ? qc : oc, la, j / NP, jj >> 1);
+    }
+  }
+
+  template <int GR, int E>
+  __device__ __forceinline__ void elem_a() {
+    constexpr int r = 8 * (GR & 1) + E;
+    const float sv = (GR >> 1) ? s1[r] : s0[r];
+    const float pv = (GR >> 1) ? p1[r] : p0[r];
+    x[E] = __builtin_fmaf(sv, scale_log2, -lq[GR & 1][E >> 2][E & 3]);
+    dd[E] = pv - dl[GR & 1][E >> 2][E & 3];
+    pin(x[E]);
+    pin(dd[E]);
+  }
+  template <int GR, int E>
+  __device__ __forceinline__ void elem_b() {
+    w[E] = __builtin_amdgcn_exp2f(x[E]);
+    pin(w[E]);
+  }
+  template <int GR, int E>
+  __device__ __forceinline__ void elem_c() {
+    g[E] = w[E] * dd[E];
+    if constexpr (E & 1) {
+      const f32x2 xw = {w[E - 1], w[E]}, yg = {g[E - 1], g[E]};
+      wp[GR & 1][E >> 1] = __builtin_convertvector(xw, bf16x2);
+      gp[GR & 1][E >> 1] = __builtin_convertvector(yg, bf16x2);
+      pin(wp[GR & 1][E >> 1]);
+      pin(gp[GR & 1][E >> 1]);
+    } else {
+      pin(g[E]);
+    }
+    if constexpr (E == 7) {
+      const bf16x2(&a)[4] = wp[GR & 1];
+      const bf16x2(&b)[4] = gp[GR & 1];
+      pb[GR] = __builtin_shufflevector(__builtin_shufflevector(a[0], a[1], 0, 1, 2, 3),
+                                       __builtin_shufflevector(a[2], a[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+      sb[GR] = __builtin_shufflevector(__builtin_shufflevector(b[0], b[1], 0, 1, 2, 3),
+                                       __builtin_shufflevector(b[2], b[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  }
+  template <int I, int GR, int... Es>
+  __device__ __forceinline__ void group_steps(std::integer_sequence<int, Es...>) {
+    ((elem_slot(GR, Es) + 2 == I ? elem_c<GR, Es>() : void()), ...);
+    ((elem_slot(GR, Es) + 1 == I ? elem_b<GR, Es>() : void()), ...);
+    ((elem_slot(GR, Es) == I ? elem_a<GR, Es>() : void()), ...);
+  }
+  template <int GR>
+  __device__ __forceinline__ void read_rows() {
+    const int rb = 16 * GR + 8 * la.hi;
+    lq[GR & 1][0] = *reinterpret_cast<const f32x4*>(lc + rb);
+    lq[GR & 1][1] = *reinterpret_cast<const f32x4*>(lc + rb + 4);
+    dl[GR & 1][0] = *reinterpret_cast<const f32x4*>(dc + rb);
+    dl[GR & 1][1] = *reinterpret_cast<const f32x4*>(dc + rb + 4);
+  }
+  __device__ __forceinline__ void mask(f32x16& sm, int off) {
+    if (masked) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qr = off + 16 * (r >> 3) + (r & 7);
+        if (qr < lo || qr > up) sm[r] = -INFINITY;
+      }
+    }
+  }
+
+  template <bool PREV, bool CUR, int I>
+  __device__ __forceinline__ void slot() {
+    constexpr int ph = I / PH, j = I % PH;
+    if constexpr (I + kLead < T && has_mfma<PREV, CUR>(I + kLead)) ring[(I + kLead) % (kLead + 1)] = frag<PREV, CUR, I + kLead>();
+    if constexpr (has_mfma<PREV, CUR>(I)) {
+      const bf16x8 A = ring[I % (kLead + 1)];
+      if constexpr (ph == 0 || ph == 2) {
+        constexpr int ks = j >> 1;
+        f32x16& c = (j & 1) ? (ph == 0 ? p0 : p1) : (ph == 0 ? s0 : s1);
+        c = mfma(A, (j & 1) ? vf[ks] : kf[ks], ks == 0 ? f32x16{} : c);
+      } else {
+        constexpr int kk = (ph == 1 ? 2 : 0) + j / NP, jj = j % NP, ct = jj >> 1;
+        if constexpr (jj & 1) dk[ct] = mfma(A, sb[kk], dk[ct]);
+        else dv[ct] = mfma(A, pb[kk], dv[ct]);
+      }
+    }
+    if constexpr (CUR && I == read_slot(0)) read_rows<0>();
+    if constexpr (CUR && I == read_slot(1)) read_rows<1>();
+    if constexpr (CUR && I == read_slot(2)) read_rows<2>();
+    if constexpr (CUR && I == read_slot(3)) read_rows<3>();
+    if constexpr (CUR && I == PH - 1) {
+      __builtin_amdgcn_sched_barrier(0);
+      mask(s0, 0);
+    }
+    if constexpr (CUR && I == 3 * PH - 1) {
+      __builtin_amdgcn_sched_barrier(0);
+      mask(s1, 32);
+    }
+    if constexpr (PREV) group_steps<I, 3>(std::make_integer_sequence<int, 8>{});
+    if constexpr (CUR) {
+      group_steps<I, 0>(std::make_integer_sequence<int, 8>{});
+      group_steps<I, 1>(std::make_integer_sequence<int, 8>{});
+      group_steps<I, 2>(std::make_integer_sequence<int, 8>{});
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  template <bool PREV, bool CUR, int... Is>
+  __device__ __forceinline__ void lead(std::integer_sequence<int, Is...>) {
+    ((has_mfma<PREV, CUR>(Is) ? (void)(ring[Is] = frag<PREV, CUR, Is>()) : void()), ...);
+  }
+  template <bool PREV, bool CUR, int... Is>
+  __device__ __forceinline__ void slots(std::integer_sequence<int, Is...>) {
+    (slot<PREV, CUR, Is>(), ...);
+  }
+  // One stage: PREV finishes the stage before (group 3 and its dV/dK for groups 2, 3), CUR runs this one. The
+  // drain (CUR false) stops after phase 1.
+  template <bool PREV, bool CUR>
+  __device__ __forceinline__ void stage() {
+    lead<PREV, CUR>(std::make_integer_sequence<int, kLead>{});
+    slots<PREV, CUR>(std::make_integer_sequence<int, CUR ? T : 2 * PH>{});
+  }
+};
+
+// ------------------------------------------------------------------------------------------------------------
 // dk/dv kernel: 128 keys of one key/value head per workgroup; query tiles of 64 of every query head in its group.
 
 // d = 64 and 128 hold K, V and both accumulators in registers at one wave per SIMD; d = 24 fits two.
@@ -588,6 +762,8 @@ void attn_bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int xcd_remap) {
   __shared__ __attribute__((aligned(16))) float rlb[kBT];
   __shared__ __attribute__((aligned(16))) float rda[kBT];
   __shared__ __attribute__((aligned(16))) float rdb[kBT];
+  __shared__ __attribute__((aligned(1024))) char qc_[D >= 64 ? G::TILE : 16];   // third tile buffers (d >= 64)
+  __shared__ __attribute__((aligned(1024))) char oc_[D >= 64 ? G::TILE : 16];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -672,25 +848,69 @@ void attn_bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int xcd_remap) {
     dv[ct] = f32x16{};
   }
 
-  // stage s: tiles in (qc, oc), converted rows in (lc, dc); the next stage's tiles go to (qn, on) and its rows
-  // are converted from the raw slot (rn_l, rn_d) into (ln, dn); the raw rows of stage s + 2 go to (rs_l, rs_d),
-  // the raw slot stage s used
-  auto step = [&](int s, const char* qc, const char* oc, const float* lc, const float* dc, char* qn, char* on,
-                  float* ln, float* dn, const float* rn_l, const float* rn_d, float* rs_l, float* rs_d) {
-    wait_vmem_all();      // this wave's copies of stage s (tiles) and s + 1 (raw rows) have landed
-    __syncthreads();      // every wave's have; every wave is done with stage s - 1
-    const bool more = s + 1 < nstages;
-    if (more) issue_stage(s + 1, qn, on);
-    if (wave == 0 && s + 2 < nstages) issue_rows(s + 2, rs_l, rs_d);
-    const int i0 = (t0 + s % nt) * kBT;
-    if (i0 + kBT - 1 >= any_lo && i0 <= any_hi)
-      DkdvStage<D>{qc, oc, lc, dc, kf, vf, dk, dv, la, a.scale_log2, !(i0 >= all_lo && i0 + kBT - 1 <= all_hi),
-                   vis_lo - i0, vis_hi - i0}();
-    if (more && wave == 0) convert_rows(s + 1, rn_l, rn_d, ln, dn);
-  };
-  for (int s = 0; s < nstages; s += 2) {
-    step(s, qa, oa, la_, da_, qb, ob, lb_, db_, rlb, rdb, rla, rda);
-    if (s + 1 < nstages) step(s + 1, qb, ob, lb_, db_, qa, oa, la_, da_, rla, rda, rlb, rdb);
+  if constexpr (D >= 64) {
+    // Stage s keeps its tiles in buffer s % 3 (it also reads stage s - 1's) and its rows in slot s % 2. After the
+    // barrier that opens stage s every wave is done with stage s - 1, so the copies of stage s + 1 may overwrite
+    // buffer (s + 1) % 3 = (s - 2) % 3. Every wave runs every stage, also one whose rows none of its keys see (the
+    // mask then hides them all): the stage after it finishes that stage's last group.
+    DkdvPipe<D> P{kf, vf, dk, dv, la, a.scale_log2};
+    auto qt = [&](int b) { return b == 0 ? qa : b == 1 ? qb : qc_; };
+    auto ot = [&](int b) { return b == 0 ? oa : b == 1 ? ob : oc_; };
+    auto run = [&](auto prev, int s, int b) {
+      wait_vmem_all();
+      __syncthreads();
+      const int bn = b == 2 ? 0 : b + 1, bp = b == 0 ? 2 : b - 1;
+      const bool more = s + 1 < nstages;
+      if (more) issue_stage(s + 1, qt(bn), ot(bn));
+      if (wave == 0 && s + 2 < nstages) issue_rows(s + 2, (s & 1) ? rlb : rla, (s & 1) ? rdb : rda);
+      const int i0 = (t0 + s % nt) * kBT;
+      P.qc = qt(b);
+      P.oc = ot(b);
+      P.qp = qt(bp);
+      P.op = ot(bp);
+      P.lc = (s & 1) ? lb_ : la_;
+      P.dc = (s & 1) ? db_ : da_;
+      P.masked = !(i0 >= all_lo && i0 + kBT - 1 <= all_hi);
+      P.lo = vis_lo - i0;
+      P.up = vis_hi - i0;
+      P.template stage<decltype(prev)::value, true>();
+      if (more && wave == 0)
+        convert_rows(s + 1, (s & 1) ? rla : rlb, (s & 1) ? rda : rdb, (s & 1) ? la_ : lb_, (s & 1) ? da_ : db_);
+    };
+    if (nstages > 0) {
+      run(std::false_type{}, 0, 0);
+      for (int s = 1; s < nstages; s += 3) {
+        run(std::true_type{}, s, 1);
+        if (s + 1 < nstages) run(std::true_type{}, s + 1, 2);
+        if (s + 2 < nstages) run(std::true_type{}, s + 2, 0);
+      }
+      // the last stage's final group and its dV/dK (its tiles stay in place: nothing more is copied)
+      const int bl = (nstages - 1) % 3;
+      P.qp = qt(bl);
+      P.op = ot(bl);
+      P.template stage<true, false>();
+    }
+  } else {
+    // stage s: tiles in (qc, oc), converted rows in (lc, dc); the next stage's tiles go to (qn, on) and its rows
+    // are converted from the raw slot (rn_l, rn_d) into (ln, dn); the raw rows of stage s + 2 go to (rs_l, rs_d),
+    // the raw slot stage s used
+    auto step = [&](int s, const char* qc, const char* oc, const float* lc, const float* dc, char* qn, char* on,
+                    float* ln, float* dn, const float* rn_l, const float* rn_d, float* rs_l, float* rs_d) {
+      wait_vmem_all();      // this wave's copies of stage s (tiles) and s + 1 (raw rows) have landed
+      __syncthreads();      // every wave's have; every wave is done with stage s - 1
+      const bool more = s + 1 < nstages;
+      if (more) issue_stage(s + 1, qn, on);
+      if (wave == 0 && s + 2 < nstages) issue_rows(s + 2, rs_l, rs_d);
+      const int i0 = (t0 + s % nt) * kBT;
+      if (i0 + kBT - 1 >= any_lo && i0 <= any_hi)
+        DkdvStage<D>{qc, oc, lc, dc, kf, vf, dk, dv, la, a.scale_log2, !(i0 >= all_lo && i0 + kBT - 1 <= all_hi),
+                     vis_lo - i0, vis_hi - i0}();
+      if (more && wave == 0) convert_rows(s + 1, rn_l, rn_d, ln, dn);
+    };
+    for (int s = 0; s < nstages; s += 2) {
+      step(s, qa, oa, la_, da_, qb, ob, lb_, db_, rlb, rdb, rla, rda);
+      if (s + 1 < nstages) step(s + 1, qb, ob, lb_, db_, qa, oa, la_, da_, rla, rda, rlb, rdb);
+    }
   }
   const int64_t kvrow = kvbh * (int64_t)a.Nk;
   store_grad<D, GF32>(reinterpret_cast<char*>(a.dk) + kvrow * D * (GF32 ? 4 : 2), kw0, a.Nk, lane, dk, a.scale,
