@@ -17,8 +17,8 @@
 //     S accumulator to the P.V MFMA without leaving the registers;
 //   * V stays row-major in LDS; the V^T operand is gathered with the LDS transpose read ds_read_b64_tr_b16
 //     (within each 16-lane group, lane i receives column i of a 4-row x 16-column block);
-//   * O is normalised by the sum of the same bf16-rounded weights that enter P.V (packed bf16 dot with (1,1));
-//     the log-sum-exp uses the sum of the fp32 weights;
+//   * O is normalised by the sum of the same bf16-rounded weights that enter P.V, formed on the matrix unit (one
+//     16x16x32 MFMA per 16 keys against a 0/1 selector); the log-sum-exp uses the sum of the fp32 weights;
 //   * the reference maximum only moves when a row's new maximum exceeds it by more than 8 (log2 units), so most
 //     tiles skip the rescale of the accumulator; the weights stay below 2^8 and the result is unchanged (the
 //     final normalisation uses the same reference).
@@ -273,7 +273,7 @@ __device__ __forceinline__ void weights_tile(float (&w)[32], bf16x8 (&pb)[4], fl
   // IEEE maximum (v_maximum3_f32): no NaN quieting of the MFMA results is needed before it.
   float mx = __builtin_elementwise_maximum(w[0], w[1]);
 #pragma unroll
-  for (int e = 2; e < 32; e += 2) mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(w[e], w[e + 1]));
+  for (int e = 2; e < 32; e += 2) mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, w[e]), w[e + 1]);
   float m_use;
   update_reference(mx, m_ref, alpha, need, m_use, scale_log2);
 #pragma unroll
@@ -282,39 +282,39 @@ __device__ __forceinline__ void weights_tile(float (&w)[32], bf16x8 (&pb)[4], fl
   for (int kk = 0; kk < 4; ++kk) pb[kk] = pack_weights(w, kk);
 }
 
-// Online softmax, second half: both running row sums. l_run sums the fp32 weights (it gives the log-sum-exp);
-// lq_run sums the bf16-rounded weights that enter P.V (one packed dot with (1, 1) per pair; it normalises O).
-// (The pair is picked with constant shuffles: reading it as element `pr` of the vector reinterpreted as four
-// 32-bit words gave element 0 for every `pr` with this compiler.)
-__device__ __forceinline__ float dot_pair(const bf16x8& v, int pr, float acc) {
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  bf16x2 x;
-  switch (pr) {
-    case 0: x = __builtin_shufflevector(v, v, 0, 1); break;
-    case 1: x = __builtin_shufflevector(v, v, 2, 3); break;
-    case 2: x = __builtin_shufflevector(v, v, 4, 5); break;
-    default: x = __builtin_shufflevector(v, v, 6, 7); break;
-  }
-  return __builtin_amdgcn_fdot2_f32_bf16(x, ones, acc, false);
+// The row sum of the bf16-rounded weights (it normalises O) on the matrix unit. pb[kk] read as the B operand of
+// a 16x16x32 MFMA holds, in lane group g = l/16 and column n = l%16, keys 8*(g/2) .. +7 of query row n + 16*(g%2)
+// of the tile's 16-key group kk. Against the selector A[m][k] = 1 if (m/4)%2 == (k/8)%2, else 0, output row m,
+// column n is the group's weight sum of query row n + 16*((m/4)%2) -- and output register i of lane l is row
+// 4*(l/16) + i, column l%16: the sum of this lane's own query row l%32, in all four registers, over both key
+// halves. (The vector ALU's packed bf16 dot instructions would take the matrix pipeline from the P.V MFMAs.)
+__device__ __forceinline__ bf16x8 rowsum_selector(int lane) {
+  const __bf16 x = (((lane & 15) >> 2) & 1) == ((lane >> 4) & 1) ? (__bf16)1.0f : (__bf16)0.0f;
+  return bf16x8{x, x, x, x, x, x, x, x};
 }
-__device__ __forceinline__ void sums_tile(const float (&w)[32], const bf16x8 (&pb)[4], float alpha, float& l_run,
-                                          float& lq_run) {
+__device__ __forceinline__ f32x4 rowsum_mfma(const bf16x8& sel, const bf16x8& p, const f32x4& acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, p, acc, 0, 0, 0);
+}
+
+// Online softmax, second half: both running row sums. l_run sums the fp32 weights (it gives the log-sum-exp);
+// lq sums the bf16-rounded weights that enter P.V (it normalises O).
+__device__ __forceinline__ void sums_tile(const float (&w)[32], const bf16x8 (&pb)[4], const bf16x8& sel, float alpha,
+                                          float& l_run, f32x4& lq) {
   float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int e = 0; e < 32; ++e) p[e & 3] += w[e];
-  float q[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int j = 0; j < 16; ++j) q[j & 3] = dot_pair(pb[j >> 2], j & 3, q[j & 3]);
   l_run = __builtin_fmaf(alpha, l_run, (p[0] + p[1]) + (p[2] + p[3]));
-  lq_run = __builtin_fmaf(alpha, lq_run, (q[0] + q[1]) + (q[2] + q[3]));
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) lq = rowsum_mfma(sel, pb[kk], lq);
 }
 
-// Rescales the accumulator when any lane's reference maximum moved.
+// Rescales the accumulator and the bf16 weight sum when any lane's reference maximum moved.
 template <int D>
-__device__ __forceinline__ void rescale_acc(f32x16 (&acc)[Geom<D>::CT], float alpha, bool need) {
+__device__ __forceinline__ void rescale_acc(f32x16 (&acc)[Geom<D>::CT], f32x4& lq, float alpha, bool need) {
   if (__builtin_amdgcn_ballot_w64(need)) {
 #pragma unroll
     for (int ct = 0; ct < Geom<D>::CT; ++ct) acc[ct] *= alpha;
+    lq *= alpha;
   }
 }
 
@@ -360,7 +360,7 @@ __device__ __forceinline__ void stage_phase1(const char* kn, const bf16x8 (&qf)[
   bf16x8 kf[kLead + 1];
 #pragma unroll
   for (int i = 0; i < kLead; ++i) kf[i] = k_frag<D>(kn, la, i);
-  float pm[4];
+  float mx = 0.0f;
 #pragma unroll
   for (int i = 0; i < NM; ++i) {
     if (i + kLead < NM) kf[(i + kLead) % (kLead + 1)] = k_frag<D>(kn, la, i + kLead);
@@ -376,15 +376,15 @@ __device__ __forceinline__ void stage_phase1(const char* kn, const bf16x8 (&qf)[
         cv.issue((i - 8) >> 1);
     }
     if (i < 4) {
-      // IEEE maximum (v_maximum3_f32): no NaN quieting of the MFMA results is needed before it.
-      float m = __builtin_elementwise_maximum(w[8 * i], w[8 * i + 1]);
+      // IEEE maximum (v_maximum3_f32): no NaN quieting of the MFMA results is needed before it. One chain over
+      // the 32 scores, two more per instruction (16 instructions; a tree of pairs takes 23).
+      float m = i == 0 ? __builtin_elementwise_maximum(w[0], w[1])
+                       : __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, w[8 * i]), w[8 * i + 1]);
 #pragma unroll
       for (int e = 2; e < 8; e += 2)
-        m = __builtin_elementwise_maximum(m, __builtin_elementwise_maximum(w[8 * i + e], w[8 * i + e + 1]));
-      pm[i] = m;
+        m = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m, w[8 * i + e]), w[8 * i + e + 1]);
+      mx = m;
     } else if (i == 4) {
-      const float mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(pm[0], pm[1]),
-                                                     __builtin_elementwise_maximum(pm[2], pm[3]));
       update_reference(mx, m_ref, alpha, need, m_use, scale_log2);
     } else if (i < 13) {
       const int e = 2 * (i - 5);
@@ -404,11 +404,12 @@ __device__ __forceinline__ void stage_phase1(const char* kn, const bf16x8 (&qf)[
 }
 
 // Phase 2: the 16 MFMAs of P.V for the current tile, beside the weights of keys 32..63 (slots 0-7), their bf16
-// rounding (slots 5, 9; each needed three slots later) and both row sums.
+// rounding (slots 5, 9; each needed three slots later) and both row sums (the bf16 one on the matrix unit in
+// slots 1, 5, 9, 13).
 template <int D>
 __device__ __forceinline__ void stage_phase2(const char* vc, f32x16 (&acc)[Geom<D>::CT], const LaneAddr<D>& la,
                                              float (&w)[32], bf16x8 (&pb)[4], float alpha, float m_use,
-                                             float scale_log2, float& l_run, float& lq_run) {
+                                             float scale_log2, float& l_run, const bf16x8& sel, f32x4& lq) {
   using G = Geom<D>;
   constexpr int NM = 4 * G::CT;
   static_assert(NM == 16, "the slot plan below is laid out for 16 MFMAs per phase");
@@ -416,7 +417,6 @@ __device__ __forceinline__ void stage_phase2(const char* vc, f32x16 (&acc)[Geom<
 #pragma unroll
   for (int j = 0; j < kLead; ++j) vf[j] = v_frag<D>(vc, la, j);
   float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  float q[2] = {0.0f, 0.0f};
 #pragma unroll
   for (int j = 0; j < NM; ++j) {
     if (j + kLead < NM) vf[(j + kLead) % (kLead + 1)] = v_frag<D>(vc, la, j + kLead);
@@ -431,14 +431,11 @@ __device__ __forceinline__ void stage_phase2(const char* vc, f32x16 (&acc)[Geom<
     }
     if (j == 5) pb[2] = pack_weights(w, 2);
     if (j == 9) pb[3] = pack_weights(w, 3);
-    // bf16 sum, one pair per slot: pb[0] and pb[1] in slots 0-7, pb[2] in slots 8-11, pb[3] in slots 12-15
-    q[j & 1] = dot_pair(pb[j >> 2], j & 3, q[j & 1]);
+    if ((j & 3) == 1) lq = rowsum_mfma(sel, pb[j >> 2], lq);
     pin(p[j & 3]);
-    pin(q[j & 1]);
     __builtin_amdgcn_sched_barrier(0);
   }
   l_run = __builtin_fmaf(alpha, l_run, (p[0] + p[1]) + (p[2] + p[3]));
-  lq_run = __builtin_fmaf(alpha, lq_run, q[0] + q[1]);
 }
 
 // Q^T fragment (B operand) of this wave's 32 rows starting at `row0` of the workgroup's block: lane holds row
@@ -466,11 +463,10 @@ __device__ __forceinline__ void load_q(const __bf16* Qblk, int rows_valid, int r
 // output may alias the running result.
 template <int D, bool OF32, bool MERGE>
 __device__ __forceinline__ void store_out(const FwdArgs& a, int64_t bh, int q0, int block_rows, int local_row, int lane,
-                                          const f32x16 (&acc)[Geom<D>::CT], float m_ref, float l_run, float lq_run) {
+                                          const f32x16 (&acc)[Geom<D>::CT], float m_ref, float l_run, float lq_tot) {
   using G = Geom<D>;
   const int hi = lane >> 5;
   const float l_tot = pair_sum(l_run);
-  const float lq_tot = pair_sum(lq_run);
   float inv = lq_tot > 0.0f ? 1.0f / lq_tot : 0.0f;
   const int qi = q0 + local_row;
   const int64_t o_rows = min(block_rows, a.Nq - q0);
@@ -610,7 +606,9 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
   f32x16 acc[G::CT];
 #pragma unroll
   for (int ct = 0; ct < G::CT; ++ct) acc[ct] = f32x16{};
-  float m_ref = -INFINITY, l_run = 0.0f, lq_run = 0.0f;
+  float m_ref = -INFINITY, l_run = 0.0f;
+  f32x4 lq = {0.0f, 0.0f, 0.0f, 0.0f};
+  const bf16x8 rsel = rowsum_selector(lane);
 
   // One tile at a time (the last tile of a wave, tiles on the diagonal, and every tile when d < 128): scores,
   // mask, weights, rescale, P.V, sums.
@@ -622,10 +620,10 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
     if (partial) mask_scores(c0, c1, row_lim - t * kBN, row_lo - t * kBN);
     unpack_scores(c0, c1, w);
     weights_tile(w, pb, m_ref, alpha, need, a.scale_log2);
-    rescale_acc<D>(acc, alpha, need);
+    rescale_acc<D>(acc, lq, alpha, need);
     __builtin_amdgcn_sched_barrier(0);
     pv_tile<D, kPipe>(vc, pb, acc, la);
-    sums_tile(w, pb, alpha, l_run, lq_run);
+    sums_tile(w, pb, rsel, alpha, l_run, lq);
   };
 
   if constexpr (kPipe) {
@@ -668,9 +666,9 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
       __builtin_amdgcn_s_setprio(1);
       stage_phase1<D>(kn, qf, n0, n1, la, w, pb, m_ref, alpha, need, m_use, a.scale_log2, ck, cv);
       __builtin_amdgcn_s_setprio(0);
-      rescale_acc<D>(acc, alpha, need);
+      rescale_acc<D>(acc, lq, alpha, need);
       __builtin_amdgcn_sched_barrier(0);
-      stage_phase2<D>(vc, acc, la, w, pb, alpha, m_use, a.scale_log2, l_run, lq_run);
+      stage_phase2<D>(vc, acc, la, w, pb, alpha, m_use, a.scale_log2, l_run, rsel, lq);
     };
     for (int t = t0; t < ntiles; t += 2) {
       stage(t, sa0, sa1, sb0, sb1, k1, k0, v0, v1);
@@ -695,7 +693,7 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
       if (t + 1 < ntiles) step(t + 1, k1, v1, k0, v0);
     }
   }
-  store_out<D, OF32, MERGE>(a, bh, q0, kRows, wave * 32 + (lane & 31), lane, acc, m_ref, l_run, lq_run);
+  store_out<D, OF32, MERGE>(a, bh, q0, kRows, wave * 32 + (lane & 31), lane, acc, m_ref, l_run, lq[0]);
 }
 
 template <int D, bool OF32, int NW>
