@@ -155,6 +155,16 @@ def bench_merge_sweep(torch, eb, dev, steps):
                      "bytes_per_launch": nbytes}
         del oa, ob, la, lb
         torch.cuda.empty_cache()
+    # the reference point of what HBM gives a plain streaming kernel: a device-to-device copy of 1.62 GB (the
+    # merge's bytes at the ring-share shape: 0.81 GB read, 0.81 GB written), torch's own copy kernel
+    n = 1623195648 // 8
+    src = torch.empty((n,), device=dev, dtype=torch.float32).fill_(1.0)
+    dst = torch.empty_like(src)
+    ms = time_region(torch, lambda: dst.copy_(src), max(steps, 10), 3)
+    out["plain_copy_1.62GB_reference"] = {"ms": ms, "GB/s": 2 * n * 4 / ms / 1e6,
+                                          "frac_hbm_peak": 2 * n * 4 / ms / 1e6 / PEAK_HBM_GBS}
+    del src, dst
+    torch.cuda.empty_cache()
     return out
 
 
