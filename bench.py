@@ -25,6 +25,7 @@ import json
 import math
 import os
 import re
+import subprocess
 import sys
 import time
 
@@ -359,6 +360,60 @@ def bench_tabular(torch, eb, dev, steps):
     return out
 
 
+def _smi_sample():
+    """One amd-smi reading of this GPU: (socket power in W, mean graphics clock over the XCDs in MHz) or None."""
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"], capture_output=True, text=True, timeout=20)
+        if r.returncode != 0:
+            return None
+        txt = r.stdout[r.stdout.find("{") if r.stdout.find("{") >= 0 else 0:]
+        d = json.loads(txt if txt.lstrip().startswith("{") else r.stdout)
+        g = (d.get("gpu_data") if isinstance(d, dict) else d)[0]
+        clks = [c["clk"]["value"] for name, c in g["clock"].items()
+                if name.startswith("gfx_") and isinstance(c, dict) and isinstance(c.get("clk"), dict)
+                and isinstance(c["clk"].get("value"), (int, float))]
+        pw = g["power"]["socket_power"]["value"]
+        if not clks or not isinstance(pw, (int, float)):
+            return None
+        return float(pw), sum(clks) / len(clks)
+    except Exception:  # no tool, other JSON layout: the reading is simply absent
+        return None
+
+
+def clock_power_under_load(torch, fn, seconds=3.0):
+    """Graphics clock and socket power while `fn` runs back to back for `seconds` (amd-smi polled from a thread;
+    the clock of a power-limited part depends on the work and the data). Medians of the readings, or None."""
+    import threading
+    readings, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            x = _smi_sample()
+            if x is not None:
+                readings.append(x)
+            stop.wait(0.1)
+
+    for _ in range(5):
+        fn()
+    torch.cuda.synchronize()
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=30)
+    if not readings:
+        return None
+    pw = sorted(r[0] for r in readings)
+    ck = sorted(r[1] for r in readings)
+    return {"gfx_clock_mhz_median": ck[len(ck) // 2], "socket_power_w_median": pw[len(pw) // 2],
+            "readings": len(readings), "seconds": seconds,
+            "how": "amd-smi metric -p -c polled while the headline step ran back to back, after the timed region"}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -453,7 +508,9 @@ def main(argv=None):
     }
     if not args.no_extra:
         try:
+            cp = clock_power_under_load(torch, step)
             result["extra"] = bench_extra(torch, eb, dev, args.steps)
+            result["extra"]["clock_power_during_headline"] = cp
         except Exception as exc:  # the headline line is printed regardless
             result["extra"] = {"error": repr(exc)}
     if not args.no_cpu:
