@@ -56,10 +56,12 @@ def compare_grad(got, ref, what, tol_norm=None, tol_max=None):
     assert err_max <= tol_max * scale, f"{what}: max error {err_max} > {tol_max} * {scale}"
 
 
-def run_case(eb, case, seed=31, o_f32=False, grad="f32"):
+def run_case(eb, case, seed=31, o_f32=False, grad="f32", q_gain=1):
     t = torch()
     B, H, Hkv, Nq, Nk, d, causal, q_off, k_off, stride, window = case
     q, k, v, do = _inputs(seed, B, H, Hkv, Nq, Nk, d)
+    if q_gain != 1:   # a power of two: the scaled bf16 values stay exact
+        q = (q.astype(np.int32) + (int(round(math.log2(q_gain))) << 7) * (q & 0x7F80 != 0)).astype(np.uint16)
     scale = 1 / math.sqrt(d)
     mask = dict(causal=causal, q_off=q_off, k_off=k_off, pos_stride=stride, window=window)
     qd, kd, vd, dod = dev_bf16(q), dev_bf16(k), dev_bf16(v), dev_bf16(do)
@@ -111,6 +113,16 @@ def test_backward_dtypes(eb, o_f32, grad):
     case = (1, 2, 1, 260, 260, 128, True, 0, 0, 1, 0)
     print(f"[case] backward dtypes o_f32={o_f32} grad={grad}", flush=True)
     run_case(eb, case, seed=32, o_f32=o_f32, grad=grad)
+
+
+@pytest.mark.parametrize("q_gain", [4, 16])
+def test_backward_peaked_softmax(eb, q_gain):
+    """Scores several times larger than N(0, 1) (q scaled by a power of two, exactly): the weights of a row
+    concentrate on a few keys and dS = P (dP - delta) nearly cancels. With o kept in fp32, delta carries no bf16
+    rounding of o, and the usual bar holds."""
+    case = (1, 2, 2, 300, 300, 128, True, 0, 0, 1, 0)
+    print(f"[case] backward peaked softmax q_gain={q_gain}", flush=True)
+    run_case(eb, case, seed=34, o_f32=True, q_gain=q_gain)
 
 
 def test_backward_ring_blocks_add_up(eb):
