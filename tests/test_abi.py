@@ -323,3 +323,20 @@ def test_ring_local_pipelined_workspace_and_validation():
     assert call(None, 2, None, 0) == eb.ATTN_EINVAL
     assert call(blocks, 3, None, 0, d=32) == eb.ATTN_EUNSUPPORTED
     assert call(blocks, 3, None, 0, B=0) == eb.ATTN_OK
+
+
+def test_import_without_the_library_fails_loudly(tmp_path):
+    """The package has no fallback: a copy of its Python files without the built library refuses to import."""
+    import os
+    import shutil
+    import sys
+    pkg = os.path.dirname(eb.__file__)
+    dst = tmp_path / "exact_blockwise_attention_amd"
+    dst.mkdir()
+    for f in os.listdir(pkg):
+        if f.endswith(".py"):
+            shutil.copy(os.path.join(pkg, f), dst / f)
+    r = subprocess.run([sys.executable, "-c", "import exact_blockwise_attention_amd"], cwd=tmp_path,
+                       capture_output=True, text=True, env={**os.environ, "PYTHONPATH": str(tmp_path)})
+    assert r.returncode != 0
+    assert "ImportError" in r.stderr and "is missing" in r.stderr and "no fallback" in r.stderr
