@@ -53,67 +53,86 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_short_kernel(FwdArgs a, int
     reinterpret_cast<u32x4*>(Vl)[e] = __builtin_nontemporal_load(Vg + src);
   }
   __syncthreads();
-  if (!live) return;
 
-
-  const __bf16* Ks = Kl + (int64_t)s * a.Nk * D;
-  const __bf16* Vs = Vl + (int64_t)s * a.Nk * D;
-  const int lim = a.causal ? min(i + a.diag, a.Nk - 1) : a.Nk - 1;   // last visible key of this row
-  const int low = a.causal ? i + a.lo : 0;                            // first key of its sliding window
-
-  // Scores with packed bf16 dot products (v_dot2_f32_bf16: two exact bf16 products added in fp32), two
-  // accumulators per key for a shorter dependency chain.
-  float sc[kShortMax];
-  float mx = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < kShortMax; ++j) {
-    sc[j] = -INFINITY;
-    if (j <= lim && j >= low) {
-      float d0 = 0.0f, d1 = 0.0f;
-#pragma unroll
-      for (int c = 0; c < D / 8; ++c) {
-        const bf16x8 kx = *reinterpret_cast<const bf16x8*>(Ks + j * D + 8 * c);
-        d0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(qv[c], qv[c], 0, 1),
-                                             __builtin_shufflevector(kx, kx, 0, 1), d0, false);
-        d1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(qv[c], qv[c], 2, 3),
-                                             __builtin_shufflevector(kx, kx, 2, 3), d1, false);
-        d0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(qv[c], qv[c], 4, 5),
-                                             __builtin_shufflevector(kx, kx, 4, 5), d0, false);
-        d1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(qv[c], qv[c], 6, 7),
-                                             __builtin_shufflevector(kx, kx, 6, 7), d1, false);
-      }
-      sc[j] = (d0 + d1) * a.scale_log2;
-      mx = fmaxf(mx, sc[j]);
-    }
-  }
+  // The output rows (one per lane, D values) go out through LDS when the workgroup's rows fit in the K/V staging
+  // area: they are one contiguous range in memory, which then leaves as full 16-byte vectors with non-temporal
+  // stores instead of each lane's short row on its own. Otherwise each lane stores its row.
+  constexpr int kOutBytes = D * (OF32 ? 4 : 2);
+  const bool stage_out = (int64_t)a.Nq * kOutBytes <= 2LL * a.Nk * D * 2;
   float acc[D];
-#pragma unroll
-  for (int c = 0; c < D; ++c) acc[c] = 0.0f;
-  float l = 0.0f;
-  if (mx != -INFINITY) {
+  float inv = 0.0f;
+  if (live) {
+    const __bf16* Ks = Kl + (int64_t)s * a.Nk * D;
+    const __bf16* Vs = Vl + (int64_t)s * a.Nk * D;
+    const int lim = a.causal ? min(i + a.diag, a.Nk - 1) : a.Nk - 1;   // last visible key of this row
+    const int low = a.causal ? i + a.lo : 0;                            // first key of its sliding window
+
+    // Scores with packed bf16 dot products (v_dot2_f32_bf16: two exact bf16 products added in fp32), two
+    // accumulators per key for a shorter dependency chain.
+    float sc[kShortMax];
+    float mx = -INFINITY;
 #pragma unroll
     for (int j = 0; j < kShortMax; ++j) {
+      sc[j] = -INFINITY;
       if (j <= lim && j >= low) {
-        const float p = __builtin_amdgcn_exp2f(sc[j] - mx);
-        l += p;
+        float d0 = 0.0f, d1 = 0.0f;
 #pragma unroll
-        for (int c = 0; c < D; c += 8) {
-          const f32x8 vx = __builtin_convertvector(*reinterpret_cast<const bf16x8*>(Vs + j * D + c), f32x8);
+        for (int c = 0; c < D / 8; ++c) {
+          const bf16x8 kx = *reinterpret_cast<const bf16x8*>(Ks + j * D + 8 * c);
+          d0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(qv[c], qv[c], 0, 1),
+                                               __builtin_shufflevector(kx, kx, 0, 1), d0, false);
+          d1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(qv[c], qv[c], 2, 3),
+                                               __builtin_shufflevector(kx, kx, 2, 3), d1, false);
+          d0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(qv[c], qv[c], 4, 5),
+                                               __builtin_shufflevector(kx, kx, 4, 5), d0, false);
+          d1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(qv[c], qv[c], 6, 7),
+                                               __builtin_shufflevector(kx, kx, 6, 7), d1, false);
+        }
+        sc[j] = (d0 + d1) * a.scale_log2;
+        mx = fmaxf(mx, sc[j]);
+      }
+    }
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[c + e] = __builtin_fmaf(p, vx[e], acc[c + e]);
+    for (int c = 0; c < D; ++c) acc[c] = 0.0f;
+    float l = 0.0f;
+    if (mx != -INFINITY) {
+#pragma unroll
+      for (int j = 0; j < kShortMax; ++j) {
+        if (j <= lim && j >= low) {
+          const float p = __builtin_amdgcn_exp2f(sc[j] - mx);
+          l += p;
+#pragma unroll
+          for (int c = 0; c < D; c += 8) {
+            const f32x8 vx = __builtin_convertvector(*reinterpret_cast<const bf16x8*>(Vs + j * D + c), f32x8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[c + e] = __builtin_fmaf(p, vx[e], acc[c + e]);
+          }
         }
       }
     }
+    inv = l > 0.0f ? 1.0f / l : 0.0f;
+    a.lse[bh * a.Nq + i] = l > 0.0f ? (mx + __builtin_amdgcn_logf(l)) * 0.69314718055994531f : -INFINITY;
   }
-  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-  a.lse[bh * a.Nq + i] = l > 0.0f ? (mx + __builtin_amdgcn_logf(l)) * 0.69314718055994531f : -INFINITY;
+  auto put = [&](unsigned char* row) {
 #pragma unroll
-  for (int c = 0; c < D; c += 4) {
-    const f32x4 y = {acc[c] * inv, acc[c + 1] * inv, acc[c + 2] * inv, acc[c + 3] * inv};
-    if (OF32)
-      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.o) + (bh * a.Nq + i) * D + c) = y;
-    else
-      *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(a.o) + (bh * a.Nq + i) * D + c) = __builtin_convertvector(y, bf16x4);
+    for (int c = 0; c < D; c += 4) {
+      const f32x4 y = {acc[c] * inv, acc[c + 1] * inv, acc[c + 2] * inv, acc[c + 3] * inv};
+      if (OF32)
+        *reinterpret_cast<f32x4*>(row + c * 4) = y;
+      else
+        *reinterpret_cast<bf16x4*>(row + c * 2) = __builtin_convertvector(y, bf16x4);
+    }
+  };
+  if (stage_out) {
+    __syncthreads();   // every lane is done reading K and V: the staging area takes the output rows
+    if (live) put(smem + (int64_t)(s * a.Nq + i) * kOutBytes);
+    __syncthreads();
+    const int nchunks = nseq * a.Nq * (kOutBytes / 16);
+    u32x4* og = reinterpret_cast<u32x4*>(reinterpret_cast<unsigned char*>(a.o) + bh0 * a.Nq * kOutBytes);
+    for (int e = tid; e < nchunks; e += kThreads)
+      __builtin_nontemporal_store(reinterpret_cast<const u32x4*>(smem)[e], og + e);
+  } else if (live) {
+    put(reinterpret_cast<unsigned char*>(a.o) + (bh * a.Nq + i) * kOutBytes);
   }
 }
 
