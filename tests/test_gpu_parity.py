@@ -91,6 +91,8 @@ def test_fp32_path_parity(eb, case):
     (2, 3, 16, 16, 64, True, 3, 0, 1),
     (1, 4, 5, 13, 128, True, 0, 4, 1),     # rows 0-3 empty
     (1000, 4, 8, 8, 24, False, 0, 0, 1),  # many slices per workgroup, ragged last workgroup
+    (7, 3, 16, 2, 64, True, 5, 0, 1),     # more output than K/V bytes: each lane stores its own row
+    (50, 2, 16, 3, 24, False, 0, 0, 1),
 ])
 @pytest.mark.parametrize("out", ["bf16", "f32"])
 def test_short_sequences(eb, case, out):
