@@ -380,6 +380,21 @@ def _smi_sample():
         return None
 
 
+def per_launch_ms(torch, fn, reps=20):
+    """Median and minimum of `reps` single launches, each bracketed by its own pair of events on the stream."""
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    fn()
+    torch.cuda.synchronize()
+    for e0, e1 in ev:
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    return {"median_ms": t[len(t) // 2], "min_ms": t[0], "launches": reps}
+
+
 def clock_power_under_load(torch, fn, seconds=3.0):
     """Graphics clock and socket power while `fn` runs back to back for `seconds` (amd-smi polled from a thread;
     the clock of a power-limited part depends on the work and the data). Medians of the readings, or None."""
@@ -508,8 +523,10 @@ def main(argv=None):
     }
     if not args.no_extra:
         try:
+            pl = per_launch_ms(torch, step)
             cp = clock_power_under_load(torch, step)
             result["extra"] = bench_extra(torch, eb, dev, args.steps)
+            result["extra"]["headline_per_launch"] = pl
             result["extra"]["clock_power_during_headline"] = cp
         except Exception as exc:  # the headline line is printed regardless
             result["extra"] = {"error": repr(exc)}
