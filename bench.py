@@ -111,6 +111,26 @@ def cpu_baseline(cfg, q_bits, k_bits, v_bits, budget_s=15.0):
                       f"(float64 numpy oracle, {elapsed:.1f} s); rate = 4*d*visible pairs / time"}
 
 
+def cpu_baseline_single_thread(cfg, q_bits, k_bits, v_bits):
+    """The same oracle on one (batch, head) slice with its BLAS limited to one thread (a per-core reference next to
+    the all-cores baseline)."""
+    import oracle
+    from workloads import accounting as acc
+    from workloads import bf16_bits_to_f64
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:
+        return None
+    q, k, v = (bf16_bits_to_f64(x[:1, :1]) for x in (q_bits, k_bits, v_bits))
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        oracle.attention(q, k, v, cfg.scale, causal=cfg.causal)
+        el = time.perf_counter() - t0
+    fl = acc.attention_flops(acc.visible_pairs(cfg.Nq, cfg.Nk_total, cfg.causal), cfg.d)
+    return {"value": fl / el / 1e12, "unit": "TFLOP/s", "cores": 1, "seconds": el,
+            "sample": f"1 (batch, head) slice of {cfg.key}, all {cfg.Nq} query rows"}
+
+
 def bench_merge(torch, eb, dev, steps):
     """LSE merge of fp32 partials in place at the ring-share shape: 32*32768 rows x d=128, 1.62 GB per launch."""
     from workloads import accounting as acc
@@ -532,6 +552,8 @@ def main(argv=None):
             result["extra"] = {"error": repr(exc)}
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(cfg, q_bits, k_bits, v_bits)
+        if "extra" in result and isinstance(result["extra"], dict):
+            result["extra"]["cpu_oracle_single_thread"] = cpu_baseline_single_thread(cfg, q_bits, k_bits, v_bits)
     print(json.dumps(result), flush=True)
     return 0
 
