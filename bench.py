@@ -464,7 +464,7 @@ def main(argv=None):
                     help="time only the attention backward (for profiling it) and print its figures as one JSON line")
     args = ap.parse_args(argv)
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this build has no "
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the library has no "
               "multi-GPU path)", file=sys.stderr)
         return 2
 
