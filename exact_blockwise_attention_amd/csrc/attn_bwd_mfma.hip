@@ -119,7 +119,8 @@ template <int D>
 __device__ __forceinline__ void copy_tile(const __bf16* X, int r0, int rows_total, char* dst, int wave, int lane) {
   using G = BG<D>;
   const int valid = uniform_clamp(rows_total - r0, kBT);
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(X + (int64_t)r0 * D, (int64_t)valid * G::RB);
+  // the range is in bytes of the rows in memory (D bf16 each), not of the padded LDS rows
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(X + (int64_t)r0 * D, (int64_t)valid * D * 2);
   const int sub = lane / G::CPR, pos = lane % G::CPR;
 #pragma unroll
   for (int i = 0; i < G::PER_WAVE; ++i) {

@@ -125,6 +125,33 @@ def test_backward_peaked_softmax(eb, q_gain):
     run_case(eb, case, seed=34, o_f32=True, q_gain=q_gain)
 
 
+@pytest.mark.parametrize("d", [24, 64, 128])
+def test_backward_reads_nothing_past_the_tensors(eb, d):
+    """Partial last tiles (166 query rows, 20 keys) with NaN right after the end of every input: rows past the end
+    must read as zeros, so the gradients stay finite and match the oracle. (At d = 24 the tile copies once sized
+    their range by the padded LDS row, 64 bytes, instead of the 48-byte row in memory, and read past the end.)"""
+    t = torch()
+    B, H, Hkv, Nq, Nk = 1, 2, 2, 166, 20
+    q, k, v, do = _inputs(35, B, H, Hkv, Nq, Nk, d)
+    print(f"[case] backward NaN-padded inputs d={d}", flush=True)
+
+    def padded(bits):
+        n = bits.size
+        buf = t.full((n + 64 * 128,), float("nan"), dtype=t.bfloat16, device="cuda")
+        buf[:n] = dev_bf16(bits).reshape(-1)
+        return buf[:n].view(bits.shape)
+
+    qd, kd, vd, dod = padded(q), padded(k), padded(v), padded(do)
+    scale = 1 / math.sqrt(d)
+    o, lse = eb.attn_fwd(qd, kd, vd, scale=scale, out_dtype=t.float32)
+    dq, dk, dv, delta = eb.attn_bwd(qd, kd, vd, o, lse, dod, scale=scale)
+    t.cuda.synchronize()
+    ref = oracle.attention_backward(bf16_bits_to_f64(q), bf16_bits_to_f64(k), bf16_bits_to_f64(v),
+                                    bf16_bits_to_f64(do), scale)
+    for name, g, r in zip(("dq", "dk", "dv", "delta"), (dq, dk, dv, delta), ref):
+        compare_grad(host_f64(g), r, f"NaN-padded d={d} {name}")
+
+
 def test_backward_ring_blocks_add_up(eb):
     """One share of a ring: the keys arrive in three blocks; with the global lse and o, the blocks' dq add up
     (accumulate) to the full dq, and each block's dk, dv are the full gradient's rows for its keys."""
