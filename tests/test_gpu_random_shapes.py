@@ -3,8 +3,10 @@
 The hand-picked cases of the other parity tests aim at known edges; this sweep draws the arguments instead
 (batch, heads and grouping, sequence lengths on both sides of the tile sizes and of the short-sequence limit,
 head dim, causal or not, offsets, stride, window, output dtype), so that combinations nobody picked are covered
-too. The draws are fixed by the seed; the bars are the same as in the other tests (bf16 inputs: 2e-2 on o,
-1e-3 on lse; fp32 inputs: 1e-5; gradients: 1e-2 normwise and 2e-2 of the largest magnitude).
+too: the forward, the backward, the fused merge (a running result over the first keys, a block over the rest)
+and the ring share (blocks of a global sequence in a drawn order, contiguous or striped, bf16 or fp32, with and
+without the exchange step). The draws are fixed by the seed; the bars are the same as in the other tests (bf16
+inputs: 2e-2 on o, 1e-3 on lse; fp32 inputs: 1e-5; gradients: 1e-2 normwise and 2e-2 of the largest magnitude).
 """
 import math
 
@@ -39,6 +41,19 @@ def _draw(rng, short_share=0.2, max_n=320):
 _RNG = np.random.default_rng(20261203)
 FWD_CASES = [(_draw(_RNG), str(_RNG.choice(["bf16", "bf16", "f32out", "f32in"]))) for _ in range(40)]
 BWD_CASES = [_draw(_RNG, short_share=0.0, max_n=260) for _ in range(16)]
+MERGE_CASES = []
+for _ in range(12):
+    _c = _draw(_RNG, short_share=0.0, max_n=300)
+    MERGE_CASES.append((_c, int(_RNG.integers(0, _c[4] + 1)), bool(_RNG.random() < 0.5)))
+RING_CASES = []
+for _ in range(12):
+    _nb = int(_RNG.integers(1, 5))
+    _f32 = bool(_RNG.random() < 0.25)
+    RING_CASES.append(dict(nb=_nb, n=int(_RNG.integers(1, 300)), d=int(_RNG.choice([24, 64, 128])),
+                           B=int(_RNG.integers(1, 3)), H=int(_RNG.choice([1, 2, 4])), causal=bool(_RNG.random() < 0.8),
+                           striped=bool(_RNG.random() < 0.3), r=int(_RNG.integers(0, _nb)), f32=_f32,
+                           pipelined=(not _f32) and bool(_RNG.random() < 0.5),
+                           order=[int(x) for x in _RNG.permutation(_nb)]))
 
 
 @pytest.fixture(scope="module")
@@ -102,3 +117,67 @@ def test_random_backward(eb, i):
                                     stride=stride, window=window)
     for name, g, r in zip(("dq", "dk", "dv", "delta"), (dq, dk, dv, delta), ref):
         compare_grad(host_f64(g), r, f"random backward {i} {case} {name}")
+
+
+@pytest.mark.parametrize("i", range(len(MERGE_CASES)),
+                         ids=[f"{_case_id(c)}-split{sp}-{'inplace' if ip else 'out'}" for c, sp, ip in MERGE_CASES])
+def test_random_fused_merge(eb, i):
+    t = torch()
+    case, split, inplace = MERGE_CASES[i]
+    B, H, Hkv, Nq, Nk, d, causal, q_off, k_off, stride, window = case
+    print(f"[case] random fused merge {i} {case} split={split} inplace={inplace}", flush=True)
+    scale = 1 / math.sqrt(d)
+    q = normal_bf16_bits(300 + i, "q", (B, H, Nq, d))
+    k = normal_bf16_bits(300 + i, "k", (B, Hkv, Nk, d))
+    v = normal_bf16_bits(300 + i, "v", (B, Hkv, Nk, d))
+    qd = dev_bf16(q)
+    k1, v1 = dev_bf16(np.ascontiguousarray(k[:, :, :split])), dev_bf16(np.ascontiguousarray(v[:, :, :split]))
+    k2, v2 = dev_bf16(np.ascontiguousarray(k[:, :, split:])), dev_bf16(np.ascontiguousarray(v[:, :, split:]))
+    run_o, run_l = eb.attn_fwd_ex(qd, k1, v1, scale=scale, causal=causal, q_off=q_off, k_off=k_off, pos_stride=stride,
+                                  window=window, out_dtype=t.float32)
+    kw = dict(scale=scale, causal=causal, q_off=q_off, k_off=k_off + split * stride, pos_stride=stride, window=window)
+    if inplace:
+        o, lse = eb.attn_fwd_merge(qd, k2, v2, run_o, run_l, out=run_o, lse=run_l, **kw)
+    else:
+        o, lse = eb.attn_fwd_merge(qd, k2, v2, run_o, run_l, **kw)
+    t.cuda.synchronize()
+    o_ref, l_ref = oracle.attention(bf16_bits_to_f64(q), bf16_bits_to_f64(k), bf16_bits_to_f64(v), scale, causal=causal,
+                                    q_off=q_off, k_off=k_off, stride=stride, window=window)
+    compare(host_f64(o), host_f64(lse), o_ref, l_ref, TOL_BF16, TOL_LSE, what=f"random fused merge {i} {case}")
+
+
+@pytest.mark.parametrize("i", range(len(RING_CASES)), ids=[
+    "nb{nb}-n{n}-d{d}-B{B}H{H}-c{causal}-{striped}-r{r}-f32{f32}-pipe{pipelined}".format(**c) for c in RING_CASES])
+def test_random_ring_share(eb, i):
+    t = torch()
+    c = RING_CASES[i]
+    nb, n, d, B, H, causal, r = c["nb"], c["n"], c["d"], c["B"], c["H"], c["causal"], c["r"]
+    print(f"[case] random ring share {i} {c}", flush=True)
+    scale = 1 / math.sqrt(d)
+    if c["striped"]:
+        offs, q_off, stride = list(range(nb)), r, nb
+    else:
+        offs, q_off, stride = [s * n for s in range(nb)], r * n, 1
+    if c["f32"]:
+        q = normal_f32(400 + i, "q", (B, H, n, d))
+        ks = [normal_f32(400 + 17 * s + i, "k", (B, H, n, d)) for s in range(nb)]
+        vs = [normal_f32(400 + 17 * s + i, "v", (B, H, n, d)) for s in range(nb)]
+        up, wide, tol, tl = dev_f32, (lambda x: x.astype(np.float64)), TOL_F32, TOL_F32
+    else:
+        q = normal_bf16_bits(400 + i, "q", (B, H, n, d))
+        ks = [normal_bf16_bits(400 + 17 * s + i, "k", (B, H, n, d)) for s in range(nb)]
+        vs = [normal_bf16_bits(400 + 17 * s + i, "v", (B, H, n, d)) for s in range(nb)]
+        up, wide, tol, tl = dev_bf16, bf16_bits_to_f64, TOL_BF16, TOL_LSE
+    blocks = [(up(ks[s]), up(vs[s]), offs[s]) for s in c["order"]]
+    if c["pipelined"]:
+        own = c["order"].index(r)
+        blocks = [blocks[own]] + [b for j, b in enumerate(blocks) if j != own]
+        o, lse = eb.ring_local_pipelined(up(q), blocks, scale=scale, causal=causal, q_off=q_off, pos_stride=stride)
+    else:
+        o, lse = eb.ring_local(up(q), blocks, scale=scale, causal=causal, q_off=q_off, pos_stride=stride)
+    t.cuda.synchronize()
+    # the share's rows of attention over all blocks: each block by the oracle, merged by the oracle's merge
+    parts = [oracle.attention(wide(q), wide(ks[s]), wide(vs[s]), scale, causal=causal, q_off=q_off, k_off=offs[s],
+                              stride=stride) for s in range(nb)]
+    o_ref, l_ref = oracle.lse_merge_many(parts)
+    compare(host_f64(o), host_f64(lse), o_ref, l_ref, tol, tl, what=f"random ring share {i}")
