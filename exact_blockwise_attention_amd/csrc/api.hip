@@ -40,30 +40,26 @@ int64_t elem_bytes(int dtype) { return dtype == ATTN_F32 ? 4 : 2; }
 bool dtype_ok(int t) { return t == ATTN_F32 || t == ATTN_BF16; }
 bool head_dim_ok(int d) { return d == 24 || d == 64 || d == 128; }
 
-// "key j visible to query i" <=> k_off + j*s <= q_off + i*s <=> j <= i + floor((q_off - k_off) / s).
-// Clamped so that every int32 expression in the kernels stays in range; with Nq, Nk <= 2^28 the clamp never
-// changes which keys are visible.
-int diag_offset(int64_t q_off, int64_t k_off, int s) {
-  const int64_t num = q_off - k_off;
-  int64_t dq = num / s;
-  if ((num % s != 0) && (num < 0)) dq -= 1;  // floor division
-  const int64_t lim = (int64_t)1 << 29;
+// floor(num / s), clamped to [-2^29, 2^29] so that every int32 expression in the kernels stays in range; with
+// Nq, Nk <= 2^28 the clamp never changes which keys are visible. num is formed in 128 bits: offsets and windows
+// of up to 2^62 in magnitude would overflow 64.
+int floor_div_clamped(__int128 num, int s) {
+  __int128 dq = num / s;
+  if ((num % s != 0) && (num < 0)) dq -= 1;
+  const __int128 lim = (__int128)1 << 29;
   if (dq > lim) dq = lim;
   if (dq < -lim) dq = -lim;
   return (int)dq;
 }
 
+// "key j visible to query i" <=> k_off + j*s <= q_off + i*s <=> j <= i + floor((q_off - k_off) / s).
+int diag_offset(int64_t q_off, int64_t k_off, int s) { return floor_div_clamped((__int128)q_off - k_off, s); }
+
 // With a sliding window of w positions, key j is also required to satisfy k_off + j*s > q_off + i*s - w, i.e.
-// j >= i + floor((q_off - k_off - w) / s) + 1. Clamped like diag_offset.
+// j >= i + floor((q_off - k_off - w) / s) + 1.
 int window_lo(int64_t q_off, int64_t k_off, int s, int64_t window) {
   if (window <= 0) return ebattn::kNoWindow;
-  const int64_t num = q_off - k_off - window;
-  int64_t dq = num / s;
-  if ((num % s != 0) && (num < 0)) dq -= 1;  // floor division
-  const int64_t lim = (int64_t)1 << 29;
-  if (dq > lim) dq = lim;
-  if (dq < -lim) dq = -lim;
-  return (int)dq + 1;
+  return floor_div_clamped((__int128)q_off - k_off - window, s) + 1;
 }
 
 const int64_t kOffLimit = (int64_t)1 << 62;

@@ -168,6 +168,21 @@ def test_ring_plan_matches_oracle_mask(causal):
         assert live == sum(k != 0 for k in want)
 
 
+def test_ring_plan_at_extreme_offsets():
+    """Offsets at the accepted limit (|offset| <= 2^62): q_off - k_off reaches 2^63, past int64, and must still
+    classify correctly (the host forms it in 128 bits)."""
+    big = 1 << 62
+    cases = [(big, -big, 1), (-big, big, 0), (big, big - 5, 2), (big - 3, big, 2), (big, big - 100, 1),
+             (-big, -big + 100, 0)]
+    for q_off, k_off, want in cases:
+        for stride in (1, 3, 4):
+            live, kinds = eb.ring_local_plan(16, [(16, k_off)], causal=1, q_off=q_off, pos_stride=stride)
+            ref = _brute_kind(16, 16, 1, q_off, k_off, stride)
+            assert kinds == [ref], (q_off, k_off, stride)
+            if stride == 1:
+                assert kinds == [want], (q_off, k_off)
+
+
 def test_ring_plan_named_workloads():
     n = 32768
     live, kinds = eb.ring_local_plan(n, [(n, 0), (n, n), (n, 2 * n), (n, 3 * n)], causal=True, q_off=2 * n)
