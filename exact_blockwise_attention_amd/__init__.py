@@ -131,6 +131,20 @@ def _stream(t) -> int:
     return _torch().cuda.current_stream(t.device).cuda_stream
 
 
+def _arg(name: str, value, bits: int = 32) -> int:
+    """value as a C integer argument of the given width (ctypes would wrap an out-of-range int silently)."""
+    v = int(value)
+    lim = 1 << (bits - 1)
+    if not -lim <= v < lim:
+        raise ValueError(f"{name} = {v} does not fit the {bits}-bit argument of the C ABI")
+    return v
+
+
+def _dims(**sizes) -> None:
+    for name, v in sizes.items():
+        _arg(name, v)
+
+
 def _need_cuda(*ts):
     for t in ts:
         if t is None:
@@ -173,8 +187,10 @@ def attn_fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False, q_
     if tuple(out.shape) != (B, H, Nq, d) or tuple(lse.shape) != (B, H, Nq) or lse.dtype != torch.float32:
         raise ValueError("out must be [B,H,Nq,d] and lse fp32 [B,H,Nq]")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _dims(B=B, H=H, Nq=Nq, Nk=Nk, d=d)
     _check(lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, d, scale, int(causal),
-                        int(q_off), int(k_off), int(pos_stride), _code(q.dtype), _code(out.dtype), _stream(q)))
+                        _arg("q_off", q_off, 64), _arg("k_off", k_off, 64), _arg("pos_stride", pos_stride),
+                        _code(q.dtype), _code(out.dtype), _stream(q)))
     return out, lse
 
 
@@ -201,8 +217,10 @@ def attn_fwd_ex(q, k, v, *, scale: Optional[float] = None, causal: bool = False,
     if tuple(out.shape) != (B, H, Nq, d) or tuple(lse.shape) != (B, H, Nq) or lse.dtype != torch.float32:
         raise ValueError("out must be [B,H,Nq,d] and lse fp32 [B,H,Nq]")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _dims(B=B, H=H, Hkv=Hkv, Nq=Nq, Nk=Nk, d=d)
     _check(lib.attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Hkv, Nq, Nk, d, scale,
-                           int(causal), int(q_off), int(k_off), int(pos_stride), int(window), _code(q.dtype),
+                           int(causal), _arg("q_off", q_off, 64), _arg("k_off", k_off, 64),
+                           _arg("pos_stride", pos_stride), _arg("window", window, 64), _code(q.dtype),
                            _code(out.dtype), _stream(q)))
     return out, lse
 
@@ -235,8 +253,10 @@ def attn_fwd_merge(q, k, v, run_o, run_lse, *, scale: Optional[float] = None, ca
     if tuple(out.shape) != (B, H, Nq, d) or tuple(lse.shape) != (B, H, Nq) or lse.dtype != torch.float32:
         raise ValueError("out must be [B,H,Nq,d] and lse fp32 [B,H,Nq]")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _dims(B=B, H=H, Hkv=Hkv, Nq=Nq, Nk=Nk, d=d)
     _check(lib.attn_fwd_merge(_ptr(q), _ptr(k), _ptr(v), _ptr(run_o), _ptr(run_lse), _ptr(out), _ptr(lse), B, H, Hkv,
-                              Nq, Nk, d, scale, int(causal), int(q_off), int(k_off), int(pos_stride), int(window),
+                              Nq, Nk, d, scale, int(causal), _arg("q_off", q_off, 64), _arg("k_off", k_off, 64),
+                              _arg("pos_stride", pos_stride), _arg("window", window, 64),
                               _code(q.dtype), _code(out.dtype), _stream(q)))
     return out, lse
 
@@ -280,10 +300,11 @@ def attn_bwd(q, k, v, o, lse, dout, *, scale: Optional[float] = None, causal: bo
     if dq.dtype != grad_dtype or dk.dtype != grad_dtype or dv.dtype != grad_dtype or delta.dtype != torch.float32:
         raise TypeError("dq, dk, dv must share grad_dtype and delta must be float32")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _dims(B=B, H=H, Hkv=Hkv, Nq=Nq, Nk=Nk, d=d)
     _check(lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
-                        _ptr(delta), B, H, Hkv, Nq, Nk, d, scale, int(causal), int(q_off), int(k_off),
-                        int(pos_stride), int(window), _code(q.dtype), _code(o.dtype), _code(grad_dtype),
-                        int(accumulate), _stream(q)))
+                        _ptr(delta), B, H, Hkv, Nq, Nk, d, scale, int(causal), _arg("q_off", q_off, 64),
+                        _arg("k_off", k_off, 64), _arg("pos_stride", pos_stride), _arg("window", window, 64),
+                        _code(q.dtype), _code(o.dtype), _code(grad_dtype), int(accumulate), _stream(q)))
     return dq, dk, dv, delta
 
 
@@ -309,12 +330,14 @@ def attn_lse_merge(o_a, lse_a, o_b, lse_b, *, out=None, lse_out=None, out_dtype=
         lse_out = torch.empty(lse_a.shape, dtype=torch.float32, device=o_a.device)
     if out.shape != o_a.shape or lse_out.shape != lse_a.shape:
         raise ValueError("out / lse_out shapes do not match the partials")
+    _dims(d=d)
     _check(lib.attn_lse_merge(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(out), _ptr(lse_out), rows, d,
                               _code(o_a.dtype), _code(out.dtype), _stream(o_a)))
     return out, lse_out
 
 
 def ring_local_workspace_bytes(B: int, H: int, Nq: int, d: int) -> int:
+    _dims(B=B, H=H, Nq=Nq, d=d)
     return int(lib.ring_local_workspace_bytes(B, H, Nq, d))
 
 
@@ -322,7 +345,7 @@ def _blocks(kv_blocks) -> Tuple[ctypes.Array, int]:
     arr = (KVBlock * max(1, len(kv_blocks)))()
     for i, (k, v, k_off) in enumerate(kv_blocks):
         if hasattr(k, "data_ptr"):
-            arr[i] = KVBlock(_ptr(k), _ptr(v), int(k.shape[2]), int(k_off))
+            arr[i] = KVBlock(_ptr(k), _ptr(v), _arg("Nk", k.shape[2]), _arg("k_off", k_off, 64))
         else:  # (k_ptr, v_ptr, Nk, k_off) raw form is not accepted here; use explicit ints via KVBlock
             raise TypeError("kv_blocks entries are (k, v, k_off) with k, v tensors")
     return arr, len(kv_blocks)
@@ -334,9 +357,10 @@ def ring_local_plan(Nq: int, blocks: Sequence[Tuple[int, int]], *, causal: bool,
     1 = fully visible, 2 = partly visible."""
     arr = (KVBlock * max(1, len(blocks)))()
     for i, (nk, ko) in enumerate(blocks):
-        arr[i] = KVBlock(None, None, int(nk), int(ko))
+        arr[i] = KVBlock(None, None, _arg("Nk", nk), _arg("k_off", ko, 64))
     kinds = (ctypes.c_int * max(1, len(blocks)))()
-    live = lib.ring_local_plan(arr, len(blocks), int(Nq), int(causal), int(q_off), int(pos_stride), kinds)
+    live = lib.ring_local_plan(arr, len(blocks), _arg("Nq", Nq), int(causal), _arg("q_off", q_off, 64),
+                               _arg("pos_stride", pos_stride), kinds)
     if live < 0:
         raise AttnError(live, last_error())
     return live, [kinds[i] for i in range(len(blocks))]
@@ -371,15 +395,17 @@ def ring_local(q_shard, kv_blocks, *, scale: Optional[float] = None, causal: boo
         workspace = torch.empty(need, dtype=torch.uint8, device=q_shard.device)
     arr, n = _blocks(kv_blocks)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _dims(B=B, H=H, Nq=Nq, d=d)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(lib.ring_local(_ptr(q_shard), arr, n, _ptr(out), _ptr(lse), B, H, Nq, d, scale, int(causal), int(q_off),
-                          int(pos_stride), _code(q_shard.dtype), _code(out.dtype), ws_ptr, ws_bytes,
-                          _stream(q_shard)))
+    _check(lib.ring_local(_ptr(q_shard), arr, n, _ptr(out), _ptr(lse), B, H, Nq, d, scale, int(causal),
+                          _arg("q_off", q_off, 64), _arg("pos_stride", pos_stride), _code(q_shard.dtype),
+                          _code(out.dtype), ws_ptr, ws_bytes, _stream(q_shard)))
     return out, lse
 
 
 def ring_local_pipelined_workspace_bytes(B: int, H: int, Nq: int, d: int, Nk_max: int) -> int:
+    _dims(B=B, H=H, Nq=Nq, d=d, Nk_max=Nk_max)
     return int(lib.ring_local_pipelined_workspace_bytes(B, H, Nq, d, Nk_max))
 
 
@@ -421,9 +447,11 @@ def ring_local_pipelined(q_shard, kv_blocks, *, scale: Optional[float] = None, c
         copy_stream = torch.cuda.Stream(device=q_shard.device)
     arr, n = _blocks(kv_blocks)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _dims(B=B, H=H, Nq=Nq, d=d)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     with torch.cuda.device(q_shard.device):   # the call creates its events on the current device
         _check(lib.ring_local_pipelined(_ptr(q_shard), arr, n, _ptr(out), _ptr(lse), B, H, Nq, d, scale,
-                                        int(causal), int(q_off), int(pos_stride), _code(out.dtype), _ptr(workspace),
-                                        ws_bytes, _stream(q_shard), copy_stream.cuda_stream))
+                                        int(causal), _arg("q_off", q_off, 64), _arg("pos_stride", pos_stride),
+                                        _code(out.dtype), _ptr(workspace), ws_bytes, _stream(q_shard),
+                                        copy_stream.cuda_stream))
     return out, lse

@@ -183,6 +183,26 @@ def test_ring_plan_at_extreme_offsets():
                 assert kinds == [want], (q_off, k_off)
 
 
+def test_binding_rejects_integers_wider_than_the_abi():
+    """ctypes reduces an int modulo 2^bits without complaint (2^64 + 5 would reach the library as 5); the binding
+    must refuse such values instead of passing a different, valid-looking argument."""
+    with pytest.raises(ValueError, match="k_off"):
+        eb.ring_local_plan(16, [(16, (1 << 64) + 5)], causal=1)
+    with pytest.raises(ValueError, match="q_off"):
+        eb.ring_local_plan(16, [(16, 0)], causal=1, q_off=-(1 << 63) - 1)
+    with pytest.raises(ValueError, match="pos_stride"):
+        eb.ring_local_plan(16, [(16, 0)], causal=1, pos_stride=(1 << 32) + 1)
+    with pytest.raises(ValueError, match="Nk"):
+        eb.ring_local_plan(16, [((1 << 32) + 16, 0)], causal=1)
+    with pytest.raises(ValueError, match="Nq"):
+        eb.ring_local_plan(1 << 31, [(16, 0)], causal=1)
+    with pytest.raises(ValueError, match="Nk_max"):
+        eb.ring_local_pipelined_workspace_bytes(1, 1, 64, 64, 1 << 40)
+    # a value that fits reaches the library unchanged, which answers with its own range check (|offset| <= 2^62)
+    with pytest.raises(eb.AttnError, match="k_off out of range"):
+        eb.ring_local_plan(16, [(16, (1 << 63) - 1)], causal=1)
+
+
 def test_ring_plan_named_workloads():
     n = 32768
     live, kinds = eb.ring_local_plan(n, [(n, 0), (n, n), (n, 2 * n), (n, 3 * n)], causal=True, q_off=2 * n)
