@@ -521,9 +521,9 @@ __device__ __forceinline__ void store_out(const FwdArgs& a, int64_t bh, int q0, 
     }
 }
 
-// Workgroup -> the (batch*head slice, query block) pairs it computes, one after another. A launch has at most
-// kMaxWorkgroups workgroups, so a workgroup's start-up (Q fragment, first K/V tiles, pipeline fill) and its
-// dispatch are paid once per several blocks. Workgroups are dispatched round-robin over the 8 XCDs; with the
+// Workgroup -> the (batch*head slice, query block) pairs it computes, one after another. At d = 128 and 64 a
+// launch has at most walk_rounds rounds of resident workgroups, so a workgroup's start-up (Q fragment, first K/V
+// tiles, pipeline fill) and its dispatch are paid once per several blocks. Workgroups are dispatched round-robin over the 8 XCDs; with the
 // remap, workgroup b serves a contiguous range of blocks, range b mod 8, so that a slice's K/V tiles are re-read
 // from one L2. A range lists its blocks slice by slice, the heaviest causal block (the last query rows) first,
 // and deals them to its workgroups in snake order: in round r, slot s takes position r*S + s when r is even and
@@ -532,8 +532,8 @@ __device__ __forceinline__ void store_out(const FwdArgs& a, int64_t bh, int q0, 
 // there every workgroup computes one block.
 template <int D>
 constexpr bool walks_blocks() { return D >= 64; }
-// Grid size in rounds of resident workgroups (measured on causal 8k: d = 128 is fastest with one round, 2 %
-// faster than one block per workgroup; d = 64 with four, 5 % faster; unmasked calls time the same either way).
+// Grid size in rounds of resident workgroups. Measured on causal 8k against one block per workgroup: d = 128 is
+// fastest with one round (0.6-2 % faster), d = 64 with four (2-5 %); unmasked calls time the same either way.
 template <int D>
 constexpr int walk_rounds() { return D >= 128 ? 1 : 4; }
 
