@@ -523,11 +523,12 @@ __device__ __forceinline__ void store_out(const FwdArgs& a, int64_t bh, int q0, 
 
 // Workgroup -> the (batch*head slice, query block) pairs it computes, one after another. At d = 128 and 64 a
 // launch has at most walk_rounds rounds of resident workgroups, so a workgroup's start-up (Q fragment, first K/V
-// tiles, pipeline fill) and its dispatch are paid once per several blocks. Workgroups are dispatched round-robin over the 8 XCDs; with the
-// remap, workgroup b serves a contiguous range of blocks, range b mod 8, so that a slice's K/V tiles are re-read
-// from one L2. A range lists its blocks slice by slice, the heaviest causal block (the last query rows) first,
-// and deals them to its workgroups in snake order: in round r, slot s takes position r*S + s when r is even and
-// r*S + S-1-s when r is odd (S workgroups per range), which pairs heavy blocks with light ones.
+// tiles, pipeline fill) and its dispatch are paid once per several blocks. Workgroups are dispatched round-robin
+// over the 8 XCDs; with the remap, workgroup b serves a contiguous range of blocks, range b mod 8, so that a
+// slice's K/V tiles are re-read from one L2. A range lists its blocks slice by slice, the heaviest causal block
+// (the last query rows) first, and deals them to its workgroups in snake order: in round r, slot s takes position
+// r*S + s when r is even and r*S + S-1-s when r is odd (S workgroups per range), which pairs heavy blocks with
+// light ones.
 // At d = 24 the loop-carried state costs more scalar registers than the exponential-bound kernel can spare;
 // there every workgroup computes one block.
 template <int D>
@@ -596,137 +597,137 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
   int64_t bh;
   int qt;
   for (int round = 0; walk.at(round, n_qtiles, bh, qt); ++round) {
-  const int q0 = qt * kRows;
-  const int64_t kvbh = bh / a.kv_group;   // the key/value head this query head reads
-  const __bf16* K = reinterpret_cast<const __bf16*>(a.k) + kvbh * (int64_t)a.Nk * D;
-  const __bf16* V = reinterpret_cast<const __bf16*>(a.v) + kvbh * (int64_t)a.Nk * D;
+    const int q0 = qt * kRows;
+    const int64_t kvbh = bh / a.kv_group;   // the key/value head this query head reads
+    const __bf16* K = reinterpret_cast<const __bf16*>(a.k) + kvbh * (int64_t)a.Nk * D;
+    const __bf16* V = reinterpret_cast<const __bf16*>(a.v) + kvbh * (int64_t)a.Nk * D;
 
-  const int qlast = min(q0 + kRows, a.Nq) - 1;
-  const int kend = a.causal ? min(a.Nk, qlast + a.diag + 1) : a.Nk;
-  const int ntiles = kend > 0 ? (kend + kBN - 1) / kBN : 0;
-  const int wrow0 = q0 + wave * 32;
-  const int wkfull = a.causal ? min(a.Nk, wrow0 + a.diag + 1) : a.Nk;
-  const int nfull = wkfull > 0 ? wkfull / kBN : 0;
-  const int wkend = a.causal ? min(a.Nk, wrow0 + 31 + a.diag + 1) : a.Nk;
+    const int qlast = min(q0 + kRows, a.Nq) - 1;
+    const int kend = a.causal ? min(a.Nk, qlast + a.diag + 1) : a.Nk;
+    const int ntiles = kend > 0 ? (kend + kBN - 1) / kBN : 0;
+    const int wrow0 = q0 + wave * 32;
+    const int wkfull = a.causal ? min(a.Nk, wrow0 + a.diag + 1) : a.Nk;
+    const int nfull = wkfull > 0 ? wkfull / kBN : 0;
+    const int wkend = a.causal ? min(a.Nk, wrow0 + 31 + a.diag + 1) : a.Nk;
 
-  // tiles this wave has any visible key in (rows past Nq may see further; they are never stored)
-  const int nt_w = min(ntiles, wkend > 0 ? (wkend + kBN - 1) / kBN : 0);
-  // Sliding window: tiles before the first key the block's first row sees are skipped; tiles before `nlow`
-  // hold keys below the window of some row of this wave and are masked.
-  const int first_key = a.causal ? q0 + a.lo : 0;
-  const int t0 = first_key > 0 ? first_key / kBN : 0;
-  const int low_edge = a.causal ? wrow0 + 31 + a.lo : 0;
-  const int nlow = low_edge > 0 ? (low_edge + kBN - 1) / kBN : 0;
-  constexpr bool kPipe = pipelined<D>();
+    // tiles this wave has any visible key in (rows past Nq may see further; they are never stored)
+    const int nt_w = min(ntiles, wkend > 0 ? (wkend + kBN - 1) / kBN : 0);
+    // Sliding window: tiles before the first key the block's first row sees are skipped; tiles before `nlow`
+    // hold keys below the window of some row of this wave and are masked.
+    const int first_key = a.causal ? q0 + a.lo : 0;
+    const int t0 = first_key > 0 ? first_key / kBN : 0;
+    const int low_edge = a.causal ? wrow0 + 31 + a.lo : 0;
+    const int nlow = low_edge > 0 ? (low_edge + kBN - 1) / kBN : 0;
+    constexpr bool kPipe = pipelined<D>();
 
-  if (ntiles > t0) {
-    issue_copy<D, true, kWaves>(K, t0 * kBN, a.Nk, k0, wave, lane);
-    issue_copy<D, false, kWaves>(V, t0 * kBN, a.Nk, v0, wave, lane);
-    if (kPipe && ntiles > t0 + 1) issue_copy<D, true, kWaves>(K, (t0 + 1) * kBN, a.Nk, k1, wave, lane);
-  }
-  bf16x8 qf[G::KSTEPS];
-  load_q<D>(reinterpret_cast<const __bf16*>(a.q) + (bh * (int64_t)a.Nq + q0) * D, min(kRows, a.Nq - q0),
-            wave * 32, lane, qf);
-  const LaneAddr<D> la(lane);
-  const int row_lim = (a.causal ? min(wrow0 + (lane & 31) + a.diag, a.Nk - 1) : a.Nk - 1) - 8 * la.hi;
-  const int row_lo = (a.causal ? wrow0 + (lane & 31) + a.lo : kNoWindow) - 8 * la.hi;
+    if (ntiles > t0) {
+      issue_copy<D, true, kWaves>(K, t0 * kBN, a.Nk, k0, wave, lane);
+      issue_copy<D, false, kWaves>(V, t0 * kBN, a.Nk, v0, wave, lane);
+      if (kPipe && ntiles > t0 + 1) issue_copy<D, true, kWaves>(K, (t0 + 1) * kBN, a.Nk, k1, wave, lane);
+    }
+    bf16x8 qf[G::KSTEPS];
+    load_q<D>(reinterpret_cast<const __bf16*>(a.q) + (bh * (int64_t)a.Nq + q0) * D, min(kRows, a.Nq - q0),
+              wave * 32, lane, qf);
+    const LaneAddr<D> la(lane);
+    const int row_lim = (a.causal ? min(wrow0 + (lane & 31) + a.diag, a.Nk - 1) : a.Nk - 1) - 8 * la.hi;
+    const int row_lo = (a.causal ? wrow0 + (lane & 31) + a.lo : kNoWindow) - 8 * la.hi;
 
-  f32x16 acc[G::CT];
-#pragma unroll
-  for (int ct = 0; ct < G::CT; ++ct) acc[ct] = f32x16{};
-  float m_ref = -INFINITY, l_run = 0.0f;
-  f32x4 lq = {0.0f, 0.0f, 0.0f, 0.0f};
-  const bf16x8 rsel = rowsum_selector(lane);
+    f32x16 acc[G::CT];
+  #pragma unroll
+    for (int ct = 0; ct < G::CT; ++ct) acc[ct] = f32x16{};
+    float m_ref = -INFINITY, l_run = 0.0f;
+    f32x4 lq = {0.0f, 0.0f, 0.0f, 0.0f};
+    const bf16x8 rsel = rowsum_selector(lane);
 
-  // One tile at a time (the last tile of a wave, tiles on the diagonal, and every tile when d < 128): scores,
-  // mask, weights, rescale, P.V, sums.
-  auto plain_tile = [&](f32x16& c0, f32x16& c1, bool partial, int t, const char* vc) {
-    float w[32];
-    bf16x8 pb[4];
-    float alpha;
-    bool need;
-    if (partial) mask_scores(c0, c1, row_lim - t * kBN, row_lo - t * kBN);
-    unpack_scores(c0, c1, w);
-    weights_tile(w, pb, m_ref, alpha, need, a.scale_log2);
-    rescale_acc<D>(acc, lq, alpha, need);
-    __builtin_amdgcn_sched_barrier(0);
-    pv_tile<D, kPipe>(vc, pb, acc, la);
-    sums_tile(w, pb, rsel, alpha, l_run, lq);
-  };
-
-  if constexpr (kPipe) {
-    // Software pipeline, one stage per tile t: the scores of tile t+1 (K tile t+1) are computed beside tile t's
-    // weights, then P.V of tile t (V tile t) beside the rest of tile t's softmax. K tiles therefore arrive one
-    // tile ahead of V tiles: after the barrier of stage t, K tile t+2 is copied into the slot of K tile t and V
-    // tile t+1 into the slot of V tile t-1.
-    f32x16 sa0, sa1, sb0, sb1;
-    wait_vmem_all();
-    __syncthreads();
-    if (nt_w > t0) qk_tile<D, true>(k0, qf, sa0, sa1, la);
-    auto stage = [&](int t, f32x16& c0, f32x16& c1, f32x16& n0, f32x16& n1, const char* kn, char* kw,
-                     const char* vc, char* vw) {
-      wait_vmem_all();      // this wave's copies of K tile t+1 and V tile t have landed
-      __syncthreads();      // so have every wave's; every wave is done with K tile t and V tile t-1
-      // K tile t+2 goes to the slot of K tile t, V tile t+1 to the slot of V tile t-1 (tiles past the end are
-      // copied as zeros, which keeps the stage free of branches; nothing reads them)
-      const TileCopy<D, true, kWaves> ck(K, (t + 2) * kBN, a.Nk, kw, wave, lane);
-      const TileCopy<D, false, kWaves> cv(V, (t + 1) * kBN, a.Nk, vw, wave, lane);
-      // A wave past its last visible tile writes zeros to n0/n1: every path then writes them, so the scores of
-      // tile t, which reach this stage in c0/c1, are dead once unpacked and are not kept beside their copy.
-      if (t >= nt_w) {
-        ck.issue_all();
-        cv.issue_all();
-        n0 = f32x16{};
-        n1 = f32x16{};
-        return;
-      }
+    // One tile at a time (the last tile of a wave, tiles on the diagonal, and every tile when d < 128): scores,
+    // mask, weights, rescale, P.V, sums.
+    auto plain_tile = [&](f32x16& c0, f32x16& c1, bool partial, int t, const char* vc) {
       float w[32];
       bf16x8 pb[4];
-      float alpha, m_use;
+      float alpha;
       bool need;
-      if (t >= nfull || t < nlow) mask_scores(c0, c1, row_lim - t * kBN, row_lo - t * kBN);
+      if (partial) mask_scores(c0, c1, row_lim - t * kBN, row_lo - t * kBN);
       unpack_scores(c0, c1, w);
-      // The wave's last tile computes the scores of one more tile, which are never used (K slot `kn` then holds
-      // an older tile): one branch-free stage shape keeps the register allocation of the loop tight.
-      __builtin_amdgcn_sched_barrier(0);
-      // Raised wave priority for phase 1: its chain (row maximum -> reference -> weights) gates the next phase,
-      // so the issue arbiter favours it over the SIMD's other wave (measured: +2.5 % causal, +0.7 % unmasked).
-      __builtin_amdgcn_s_setprio(1);
-      stage_phase1<D>(kn, qf, n0, n1, la, w, pb, m_ref, alpha, need, m_use, a.scale_log2, ck, cv);
-      __builtin_amdgcn_s_setprio(0);
+      weights_tile(w, pb, m_ref, alpha, need, a.scale_log2);
       rescale_acc<D>(acc, lq, alpha, need);
       __builtin_amdgcn_sched_barrier(0);
-      stage_phase2<D>(vc, acc, la, w, pb, alpha, m_use, a.scale_log2, l_run, rsel, lq);
+      pv_tile<D, kPipe>(vc, pb, acc, la);
+      sums_tile(w, pb, rsel, alpha, l_run, lq);
     };
-    for (int t = t0; t < ntiles; t += 2) {
-      stage(t, sa0, sa1, sb0, sb1, k1, k0, v0, v1);
-      if (t + 1 < ntiles) stage(t + 1, sb0, sb1, sa0, sa1, k0, k1, v1, v0);
-    }
-  } else {
-    // One tile per step: after the barrier of tile t, tile t+1 is copied into the slots tile t-1 left.
-    auto step = [&](int t, const char* kc, const char* vc, char* kn, char* vn) {
-      wait_vmem_all();      // this wave's copies of tile t have landed
-      __syncthreads();      // every wave's copies have landed; every wave is done with tile t-1
-      if (t + 1 < ntiles) {
-        issue_copy<D, true, kWaves>(K, (t + 1) * kBN, a.Nk, kn, wave, lane);
-        issue_copy<D, false, kWaves>(V, (t + 1) * kBN, a.Nk, vn, wave, lane);
+
+    if constexpr (kPipe) {
+      // Software pipeline, one stage per tile t: the scores of tile t+1 (K tile t+1) are computed beside tile t's
+      // weights, then P.V of tile t (V tile t) beside the rest of tile t's softmax. K tiles therefore arrive one
+      // tile ahead of V tiles: after the barrier of stage t, K tile t+2 is copied into the slot of K tile t and V
+      // tile t+1 into the slot of V tile t-1.
+      f32x16 sa0, sa1, sb0, sb1;
+      wait_vmem_all();
+      __syncthreads();
+      if (nt_w > t0) qk_tile<D, true>(k0, qf, sa0, sa1, la);
+      auto stage = [&](int t, f32x16& c0, f32x16& c1, f32x16& n0, f32x16& n1, const char* kn, char* kw,
+                       const char* vc, char* vw) {
+        wait_vmem_all();      // this wave's copies of K tile t+1 and V tile t have landed
+        __syncthreads();      // so have every wave's; every wave is done with K tile t and V tile t-1
+        // K tile t+2 goes to the slot of K tile t, V tile t+1 to the slot of V tile t-1 (tiles past the end are
+        // copied as zeros, which keeps the stage free of branches; nothing reads them)
+        const TileCopy<D, true, kWaves> ck(K, (t + 2) * kBN, a.Nk, kw, wave, lane);
+        const TileCopy<D, false, kWaves> cv(V, (t + 1) * kBN, a.Nk, vw, wave, lane);
+        // A wave past its last visible tile writes zeros to n0/n1: every path then writes them, so the scores of
+        // tile t, which reach this stage in c0/c1, are dead once unpacked and are not kept beside their copy.
+        if (t >= nt_w) {
+          ck.issue_all();
+          cv.issue_all();
+          n0 = f32x16{};
+          n1 = f32x16{};
+          return;
+        }
+        float w[32];
+        bf16x8 pb[4];
+        float alpha, m_use;
+        bool need;
+        if (t >= nfull || t < nlow) mask_scores(c0, c1, row_lim - t * kBN, row_lo - t * kBN);
+        unpack_scores(c0, c1, w);
+        // The wave's last tile computes the scores of one more tile, which are never used (K slot `kn` then holds
+        // an older tile): one branch-free stage shape keeps the register allocation of the loop tight.
+        __builtin_amdgcn_sched_barrier(0);
+        // Raised wave priority for phase 1: its chain (row maximum -> reference -> weights) gates the next phase,
+        // so the issue arbiter favours it over the SIMD's other wave (measured: +2.5 % causal, +0.7 % unmasked).
+        __builtin_amdgcn_s_setprio(1);
+        stage_phase1<D>(kn, qf, n0, n1, la, w, pb, m_ref, alpha, need, m_use, a.scale_log2, ck, cv);
+        __builtin_amdgcn_s_setprio(0);
+        rescale_acc<D>(acc, lq, alpha, need);
+        __builtin_amdgcn_sched_barrier(0);
+        stage_phase2<D>(vc, acc, la, w, pb, alpha, m_use, a.scale_log2, l_run, rsel, lq);
+      };
+      for (int t = t0; t < ntiles; t += 2) {
+        stage(t, sa0, sa1, sb0, sb1, k1, k0, v0, v1);
+        if (t + 1 < ntiles) stage(t + 1, sb0, sb1, sa0, sa1, k0, k1, v1, v0);
       }
-      if (t >= nt_w) return;
-      f32x16 s0, s1;
-      qk_tile<D>(kc, qf, s0, s1, la);
-      plain_tile(s0, s1, t >= nfull || t < nlow, t, vc);
-    };
-    for (int t = t0; t < ntiles; t += 2) {
-      step(t, k0, v0, k1, v1);
-      if (t + 1 < ntiles) step(t + 1, k1, v1, k0, v0);
+    } else {
+      // One tile per step: after the barrier of tile t, tile t+1 is copied into the slots tile t-1 left.
+      auto step = [&](int t, const char* kc, const char* vc, char* kn, char* vn) {
+        wait_vmem_all();      // this wave's copies of tile t have landed
+        __syncthreads();      // every wave's copies have landed; every wave is done with tile t-1
+        if (t + 1 < ntiles) {
+          issue_copy<D, true, kWaves>(K, (t + 1) * kBN, a.Nk, kn, wave, lane);
+          issue_copy<D, false, kWaves>(V, (t + 1) * kBN, a.Nk, vn, wave, lane);
+        }
+        if (t >= nt_w) return;
+        f32x16 s0, s1;
+        qk_tile<D>(kc, qf, s0, s1, la);
+        plain_tile(s0, s1, t >= nfull || t < nlow, t, vc);
+      };
+      for (int t = t0; t < ntiles; t += 2) {
+        step(t, k0, v0, k1, v1);
+        if (t + 1 < ntiles) step(t + 1, k1, v1, k0, v0);
+      }
     }
-  }
-  store_out<D, OF32, MERGE>(a, bh, q0, kRows, wave * 32 + (lane & 31), lane, acc, m_ref, l_run, lq[0]);
-  if constexpr (!walks_blocks<D>()) break;
-  // Every wave is done reading the LDS slots (its last reads fed the products just stored) before any wave copies
-  // the next block's first tiles into them. A wave's copies land in issue order and each wave fills the same rows
-  // of a slot every time, so the unused tiles the last stages copied cannot overwrite the new ones.
-  __builtin_amdgcn_s_barrier();
+    store_out<D, OF32, MERGE>(a, bh, q0, kRows, wave * 32 + (lane & 31), lane, acc, m_ref, l_run, lq[0]);
+    if constexpr (!walks_blocks<D>()) break;
+    // Every wave is done reading the LDS slots (its last reads fed the products just stored) before any wave copies
+    // the next block's first tiles into them. A wave's copies land in issue order and each wave fills the same rows
+    // of a slot every time, so the unused tiles the last stages copied cannot overwrite the new ones.
+    __builtin_amdgcn_s_barrier();
   }
 }
 
