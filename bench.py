@@ -1,6 +1,7 @@
 """Benchmark of the exact blockwise attention forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu] [--copy-probe BYTES] [--merge-only] [--bwd-only]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu] [--no-counters] [--copy-probe BYTES]
+                    [--merge-only | --bwd-only | --rows-only | --profile {fwd,bwd,merge,rows} --profile-out DIR]
 
 A step is one attention forward (scores, causal mask by position, online softmax, P.V, epilogue) over the
 causal self-attention workload B=4, H=32, N=8192, d=128, bf16 in / bf16 out with fp32 lse, inputs iid N(0,1)
@@ -267,12 +268,32 @@ def bench_extra(torch, eb, dev, steps):
     return out
 
 
+def isolated_ms(torch, fn, reps, warmup=1):
+    """Mean of `reps` calls, each alone on the device: synchronised before, timed by its own pair of events on the
+    current stream (nothing of the previous call can overlap it)."""
+    for _ in range(warmup):
+        fn()
+    stream = torch.cuda.current_stream()
+    total = 0.0
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        total += e0.elapsed_time(e1)
+    return total / reps
+
+
 def bench_ring_pipeline(torch, eb, dev, c3, qd, kd, vd, order, ms_compute, fl, steps):
     """The ring share with its exchange step on this GPU (ring_local_pipelined): the resident block is read in
     place, every incoming live block is copied from pinned host memory (the stand-in for the neighbour's link;
     over PCIe, by the copy engines) into a receive slot on a second stream while the compute stream attends the
-    block before it. Reported beside the compute alone (ring_local, all blocks resident) and the copies alone:
-    hidden = (compute + copies - pipelined) / copies is the share of the transfer time hidden under compute."""
+    block before it. Every call runs alone (device synchronised before it), and so do the references: the compute
+    alone (ring_local, all blocks resident) and the copies alone. hidden = (compute + copies - pipelined) / copies
+    is the share of the transfer time hidden under compute; the first incoming block can only hide under the
+    resident block's attention, which bounds it."""
     n = c3.Nq
     live = [s for s in order if s * n <= c3.q_off + n - 1]            # blocks a causal share sees at all
     host = {s: (kd[s].cpu().pin_memory(), vd[s].cpu().pin_memory()) for s in live[1:]}
@@ -281,16 +302,20 @@ def bench_ring_pipeline(torch, eb, dev, c3, qd, kd, vd, order, ms_compute, fl, s
     o = torch.empty_like(qd)
     lse = torch.empty((c3.B, c3.H, n), dtype=torch.float32, device=dev)
     cstream = torch.cuda.Stream(device=dev)
-    ms_pipe = time_region(torch, lambda: eb.ring_local_pipelined(qd, blocks, causal=True, q_off=c3.q_off, out=o, lse=lse,
-                                                                 workspace=ws, copy_stream=cstream),
-                          max(2, steps // 4), 1)
+    reps = max(2, steps // 4)
+    ms_pipe = isolated_ms(torch, lambda: eb.ring_local_pipelined(qd, blocks, causal=True, q_off=c3.q_off, out=o,
+                                                                 lse=lse, workspace=ws, copy_stream=cstream), reps)
+    ws_all = torch.empty(eb.ring_local_workspace_bytes(c3.B, c3.H, n, c3.d), dtype=torch.uint8, device=dev)
+    resident = [(kd[s], vd[s], s * n) for s in order]
+    ms_compute = isolated_ms(torch, lambda: eb.ring_local(qd, resident, causal=True, q_off=c3.q_off, out=o, lse=lse,
+                                                          workspace=ws_all), reps)
     recv = [torch.empty_like(kd[0]) for _ in range(2)]
 
     def copies():
         for s in live[1:]:
             recv[0].copy_(host[s][0], non_blocking=True)
             recv[1].copy_(host[s][1], non_blocking=True)
-    ms_copy = time_region(torch, copies, max(2, steps // 4), 1)
+    ms_copy = isolated_ms(torch, copies, reps)
     nbytes = sum(host[s][0].numel() * 2 * 2 for s in live[1:])
     return {"ms": ms_pipe, "TFLOP/s": fl / ms_pipe / 1e9, "ms_compute_only": ms_compute, "ms_copies_only": ms_copy,
             "copy_GB/s": nbytes / ms_copy / 1e6, "bytes_copied": nbytes,
@@ -351,11 +376,10 @@ def bench_backward(torch, eb, dev, steps):
                      max(steps, 10), 2)
     fl = acc.attention_backward_flops(B * H * acc.visible_pairs(N, N, True), d)
     return {"attn_bwd_causal_8k_d128": {"ms": ms, "TFLOP/s": fl / ms / 1e9,
-                                        "frac_mfma_peak": fl / ms / 1e9 / PEAK_BF16_TFLOPS,
-                                        "mfma_TFLOP/s_executed": 1.4 * fl / ms / 1e9}}
+                                        "frac_mfma_peak": fl / ms / 1e9 / PEAK_BF16_TFLOPS}}
 
 
-def bench_tabular(torch, eb, dev, steps):
+def bench_tabular(torch, eb, dev, steps, rows_only=False):
     """The tabular stand-in, both axes of one (1, 150000, 8, 4, 24) tensor: the row axis (8*4 sequences of
     150000 tokens, d = 24, bound by the exponential and vector ALU work) and the feature axis (600000 sequences of
     8 tokens, HBM-bound). The permutation between the two layouts happens outside the timed region."""
@@ -368,6 +392,8 @@ def bench_tabular(torch, eb, dev, steps):
     ms = time_region(torch, lambda: eb.attn_fwd(q, k, v, scale=cr.scale, out=o, lse=lse), max(2, steps // 4), 1)
     fl = acc.attention_flops(acc.config_pairs(cr), cr.d)
     out = {"tabular_rows_150k_d24": {"ms": ms, "TFLOP/s": fl / ms / 1e9, "frac_mfma_peak": fl / ms / 1e9 / PEAK_BF16_TFLOPS}}
+    if rows_only:
+        return out
     cf = CONFIGS["tabular_features_8"]
     qf, kf, vf = (x.permute(2, 1, 0, 3).contiguous() for x in (q, k, v))   # -> [rows, heads, features, d]
     del q, k, v, o, lse
@@ -449,6 +475,156 @@ def clock_power_under_load(torch, fn, seconds=3.0):
             "how": "amd-smi metric -p -c polled while the headline step ran back to back, after the timed region"}
 
 
+# ------------------------------------------------------------------------------------------------------------
+# rocprofv3 passes over a child run of one kind of step. The child is this script with the step alone; its kernels
+# are found by name in the CSV files rocprofv3 writes. Counter values are per dispatch, summed over the chip by
+# rocprofv3: GRBM_GUI_ACTIVE over its 8 XCDs (cycles the GPU was busy, per XCD, once divided), the SQ cycle
+# counters over the 1024 SIMDs.
+N_XCD, N_SIMD = 8, 1024
+SQ_COUNTERS = ["SQ_WAVES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA",
+               "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_LDS", "SQ_WAIT_INST_LDS", "GRBM_GUI_ACTIVE"]
+# second pass: executed bf16 MFMA work (512 FLOP per counted op), transcendental instructions (one per lane per
+# wave instruction), vector-ALU issue cycles and waits
+SQ_COUNTERS_2 = ["SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_TRANS_F32", "SQ_ACTIVE_INST_VALU", "SQ_WAIT_ANY",
+                 "GRBM_GUI_ACTIVE"]
+# step kind -> (child arguments, kernel-name substrings to report, steps, warmup)
+PROFILE_TARGETS = {
+    "fwd": (["--no-extra", "--no-cpu"], ["attn_fwd_kernel<128"], 20, 3),
+    "bwd": (["--bwd-only"], ["attn_bwd_dq_kernel<128", "attn_bwd_dkdv_kernel<128"], 10, 2),
+    "merge": (["--merge-only"], ["lse_merge_kernel"], 20, 3),
+    "rows": (["--rows-only"], ["attn_fwd_kernel<24"], 4, 1),
+}
+
+
+def _rocprof_child(kind, mode, outdir, steps, warmup, extra_args=(), limit_s=240):
+    """Runs one rocprofv3 pass (mode: ["--kernel-trace", "--stats"] or ["--pmc", counters...]) over this script's
+    `kind` step in a child process; returns (the command as text, rc)."""
+    import shutil
+    exe = shutil.which("rocprofv3")
+    if exe is None:
+        return "rocprofv3 not found", 127
+    child, _, _, _ = PROFILE_TARGETS[kind]
+    os.makedirs(outdir, exist_ok=True)
+    prog = [sys.executable, "-u", os.path.join(ROOT, "bench.py"), *child, "--no-counters", "--steps", str(steps),
+            "--warmup", str(warmup), *extra_args]
+    cmd = [exe, *mode, "-f", "csv", "-d", outdir, "-o", "p", "--", *prog]
+    env = dict(os.environ)
+    env.setdefault("TMPDIR", "/tmp")
+    with open(os.path.join(outdir, "child.log"), "w") as logf:
+        try:
+            r = subprocess.run(["timeout", "-k", "10", "-s", "KILL", str(limit_s), *cmd], stdout=logf,
+                               stderr=subprocess.STDOUT, env=env, cwd=env["TMPDIR"])
+            rc = r.returncode
+        except OSError as exc:
+            logf.write(repr(exc))
+            rc = 126
+    shown = " ".join(["rocprofv3", *mode, "-f", "csv", "-d", "<out>", "-o", "p", "--", "python", "-u", "bench.py",
+                      *prog[3:]])
+    return shown, rc
+
+
+def _csv_rows(outdir, suffix):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(outdir, "**", f"*{suffix}"), recursive=True)):
+        with open(f, newline="") as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def trace_durations(outdir, substr, last):
+    """Durations (ns) of the last `last` dispatches of the kernel whose name contains `substr`, in dispatch order."""
+    rows = [r for r in _csv_rows(outdir, "kernel_trace.csv") if substr in r.get("Kernel_Name", "")]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    return [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows][-last:]
+
+
+def counter_dispatches(outdir, substr):
+    """Per dispatch of the kernel whose name contains `substr`: {counter: value, "_ns": duration if recorded}."""
+    per = {}
+    for r in _csv_rows(outdir, "counter_collection.csv"):
+        if substr not in r.get("Kernel_Name", ""):
+            continue
+        key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+        d = per.setdefault(key, {})
+        name = r.get("Counter_Name")
+        d[name] = d.get(name, 0.0) + float(r.get("Counter_Value", "nan"))
+        if r.get("Start_Timestamp") and r.get("End_Timestamp"):
+            d["_ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    return [per[k] for k in sorted(per, key=lambda x: int(x))]
+
+
+def derive_sq(c, c2, kernel_ns):
+    """MFMA-busy fraction, clock and instruction mix from one dispatch's SQ / GRBM counters (c: first pass, c2:
+    second pass or None); kernel_ns is the kernel's duration from the trace pass."""
+    active = c["GRBM_GUI_ACTIVE"] / N_XCD                       # busy cycles of one XCD's clock
+    out = {"mfma_busy": c["SQ_VALU_MFMA_BUSY_CYCLES"] / N_SIMD / active,
+           "valu_per_mfma": c["SQ_INSTS_VALU"] / max(1.0, c["SQ_INSTS_MFMA"]),
+           "lds_per_mfma": c["SQ_INSTS_LDS"] / max(1.0, c["SQ_INSTS_MFMA"]),
+           "lds_wait_per_wave_cycle": c["SQ_WAIT_INST_LDS"] / max(1.0, c["SQ_WAVE_CYCLES"]),
+           "mfma_instructions": c["SQ_INSTS_MFMA"], "active_cycles_per_xcd": active,
+           "clock_ghz": active / kernel_ns}
+    if c2:
+        out["mfma_flop_executed"] = c2["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+        out["mfma_tflops_executed"] = out["mfma_flop_executed"] / kernel_ns / 1e3
+        out["exp_lane_ops"] = c2["SQ_INSTS_VALU_TRANS_F32"] * 64
+        out["valu_active_per_simd_cycle"] = c2["SQ_ACTIVE_INST_VALU"] / N_SIMD / (c2["GRBM_GUI_ACTIVE"] / N_XCD)
+    return out
+
+
+def profile_kind(kind, outdir, traffic=False, limit_s=240):
+    """Kernel trace, SQ counters and (with traffic) the FETCH_SIZE / WRITE_SIZE passes of one step kind. Returns
+    {"commands": [...], kernel substring: {figures}} or {"error": ...}."""
+    _, kernels, steps, warmup = PROFILE_TARGETS[kind]
+    res = {"commands": []}
+    cmd, rc = _rocprof_child(kind, ["--kernel-trace", "--stats"], os.path.join(outdir, "trace"), steps, warmup,
+                             limit_s=limit_s)
+    res["commands"].append(cmd)
+    if rc != 0:
+        return {"error": f"trace pass rc={rc}", **res}
+    for sub_dir, ctrs in (("sq", SQ_COUNTERS), ("sq2", SQ_COUNTERS_2)):
+        cmd, rc = _rocprof_child(kind, ["--pmc", *ctrs], os.path.join(outdir, sub_dir), 2, 1, limit_s=limit_s)
+        res["commands"].append(cmd)
+        if rc != 0:
+            return {"error": f"counter pass {sub_dir} rc={rc}", **res}
+    for sub in kernels:
+        durs = trace_durations(os.path.join(outdir, "trace"), sub, steps)
+        disp = counter_dispatches(os.path.join(outdir, "sq"), sub)
+        if not durs or not disp:
+            res[sub] = {"error": "kernel not found in the rocprofv3 output"}
+            continue
+        ns = sum(durs) / len(durs)
+        fig = {"dispatches_timed": len(durs), "kernel_ns_avg": ns, "kernel_ns_median": sorted(durs)[len(durs) // 2]}
+        c = disp[-1]
+        d2 = counter_dispatches(os.path.join(outdir, "sq2"), sub)
+        c2 = d2[-1] if d2 else None
+        fig.update(derive_sq(c, c2, ns))
+        fig["counters"] = {k: v for k, v in c.items() if not k.startswith("_")}
+        if c2:
+            fig["counters"].update({k: v for k, v in c2.items() if not k.startswith("_")})
+        res[sub] = fig
+    if traffic:
+        cal = 1 << 30
+        for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+            cmd, rc = _rocprof_child(kind, ["--pmc", ctr], os.path.join(outdir, ctr.lower()), 2, 1,
+                                     ["--copy-probe", str(cal)], limit_s=limit_s)
+            res["commands"].append(cmd)
+            if rc != 0:
+                return {"error": f"{ctr} pass rc={rc}", **res}
+            # torch's plain device copy of `cal` bytes (the --copy-probe step) reads cal and writes cal bytes: the
+            # counter's scale is bytes per counted KiB of that dispatch
+            copy = [d for d in counter_dispatches(os.path.join(outdir, ctr.lower()), "copy") if ctr in d]
+            copy_kib = max((d[ctr] for d in copy), default=None)
+            for sub in kernels:
+                ks = counter_dispatches(os.path.join(outdir, ctr.lower()), sub)
+                if ks and copy_kib and isinstance(res.get(sub), dict):
+                    scale = cal / (copy_kib * 1024)
+                    res[sub][ctr.lower() + "_bytes"] = sum(d[ctr] for d in ks) / len(ks) * 1024 * scale
+                    res[sub][ctr.lower() + "_scale"] = scale
+    return res
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -462,11 +638,25 @@ def main(argv=None):
                     help="time only the LSE merge (for profiling it) and print its figures as one JSON line")
     ap.add_argument("--bwd-only", action="store_true",
                     help="time only the attention backward (for profiling it) and print its figures as one JSON line")
+    ap.add_argument("--rows-only", action="store_true",
+                    help="time only the tabular row axis (d = 24) and print its figures as one JSON line")
+    ap.add_argument("--no-counters", action="store_true",
+                    help="skip the rocprofv3 passes (kernel trace, SQ counters) over a child run of the headline step")
+    ap.add_argument("--profile", choices=sorted(PROFILE_TARGETS),
+                    help="only run the rocprofv3 passes (trace, SQ counters, HBM traffic) of one step kind into "
+                         "--profile-out and print their figures as one JSON line")
+    ap.add_argument("--profile-out", default=os.path.join(ROOT, "gpurun_out", "profile"))
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the library has no "
               "multi-GPU path)", file=sys.stderr)
         return 2
+
+    if args.profile:
+        res = profile_kind(args.profile, os.path.join(args.profile_out, args.profile), traffic=True)
+        res["kernel_source_sha256_16"] = kernel_hash()
+        print(json.dumps(res), flush=True)
+        return 0 if "error" not in res else 1
 
     import torch
     import exact_blockwise_attention_amd as eb
@@ -488,6 +678,9 @@ def main(argv=None):
         return 0
     if args.bwd_only:
         print(json.dumps(bench_backward(torch, eb, dev, args.steps)), flush=True)
+        return 0
+    if args.rows_only:
+        print(json.dumps(bench_tabular(torch, eb, dev, args.steps, rows_only=True)), flush=True)
         return 0
     cfg = CONFIGS["causal_8k"]
     t0 = time.perf_counter()
@@ -541,6 +734,31 @@ def main(argv=None):
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "kernel": "attn_fwd_kernel<128,bf16 out>", "kernel_source_sha256_16": kernel_hash()},
     }
+    if not args.no_counters:
+        # the same step under rocprofv3 in a child process, on this GPU, right after the timed region: the kernel's
+        # own duration from the trace, and MFMA busy / clock / instruction mix from the SQ counters
+        import tempfile
+        torch.cuda.synchronize()
+        log("[bench] rocprofv3 passes over a child run of the headline step")
+        t_p = time.perf_counter()
+        prof = profile_kind("fwd", tempfile.mkdtemp(prefix="ebattn_prof_"), traffic=False)
+        fig = prof.get("attn_fwd_kernel<128")
+        if isinstance(fig, dict) and "error" not in fig and "error" not in prof:
+            rf = result["roofline"]
+            rf["kernel_ns_rocprof"] = round(fig["kernel_ns_avg"])
+            rf["frac_at_rocprof_kernel_time"] = round(flops / fig["kernel_ns_avg"] / 1e3 / PEAK_BF16_TFLOPS, 4)
+            rf["mfma_busy"] = round(fig["mfma_busy"], 4)
+            rf["clock_ghz"] = round(fig["clock_ghz"], 3)
+            rf["peak_at_clock"] = round(PEAK_BF16_TFLOPS * fig["clock_ghz"] / 2.4, 1)
+            rf["valu_per_mfma"] = round(fig["valu_per_mfma"], 3)
+            if "mfma_tflops_executed" in fig:
+                rf["mfma_tflops_executed"] = round(fig["mfma_tflops_executed"], 1)
+                rf["valu_active_per_simd_cycle"] = round(fig["valu_active_per_simd_cycle"], 4)
+            rf["counters_from"] = ("rocprofv3 child passes on this GPU after the timed region: " +
+                                   "; ".join(prof["commands"]))
+        else:
+            result["roofline"]["counters_error"] = str(prof.get("error") or fig)
+        log(f"[bench] rocprofv3 passes done in {time.perf_counter() - t_p:.1f} s")
     if not args.no_extra:
         try:
             pl = per_launch_ms(torch, step)

@@ -404,6 +404,17 @@ def ring_local(q_shard, kv_blocks, *, scale: Optional[float] = None, causal: boo
     return out, lse
 
 
+# Host (pinned) blocks handed to ring_local_pipelined are read by the copy engines after the call returns. Each
+# call's host tensors stay referenced here, with an event recorded on the compute stream after the call, until that
+# event has completed: torch's pinned-memory cache cannot hand their pages to a new tensor while a copy still reads
+# them.
+_inflight_host_blocks: List[Tuple[object, List[object]]] = []
+
+
+def _retire_host_blocks() -> None:
+    _inflight_host_blocks[:] = [(ev, ts) for ev, ts in _inflight_host_blocks if not ev.query()]
+
+
 def ring_local_pipelined_workspace_bytes(B: int, H: int, Nq: int, d: int, Nk_max: int) -> int:
     _dims(B=B, H=H, Nq=Nq, d=d, Nk_max=Nk_max)
     return int(lib.ring_local_pipelined_workspace_bytes(B, H, Nq, d, Nk_max))
@@ -449,9 +460,15 @@ def ring_local_pipelined(q_shard, kv_blocks, *, scale: Optional[float] = None, c
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     _dims(B=B, H=H, Nq=Nq, d=d)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _retire_host_blocks()
     with torch.cuda.device(q_shard.device):   # the call creates its events on the current device
         _check(lib.ring_local_pipelined(_ptr(q_shard), arr, n, _ptr(out), _ptr(lse), B, H, Nq, d, scale,
                                         int(causal), _arg("q_off", q_off, 64), _arg("pos_stride", pos_stride),
                                         _code(out.dtype), _ptr(workspace), ws_bytes, _stream(q_shard),
                                         copy_stream.cuda_stream))
+        host = [t for k, v, _ in kv_blocks for t in (k, v) if not t.is_cuda]
+        if host:
+            ev = torch.cuda.Event()
+            ev.record(torch.cuda.current_stream(q_shard.device))
+            _inflight_host_blocks.append((ev, host))
     return out, lse

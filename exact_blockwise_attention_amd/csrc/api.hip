@@ -394,10 +394,14 @@ int ring_local_plan(const attn_kv_block* kv_blocks, int n_blocks, int Nq, int ca
   return live;
 }
 
-int ring_local(const void* q_shard, const attn_kv_block* kv_blocks, int n_blocks, void* o, float* lse, int B, int H,
-               int Nq, int d, float scale, int causal, int64_t q_off, int pos_stride, int in_dtype, int o_dtype,
-               void* workspace, size_t workspace_bytes, void* stream) {
-  g_err[0] = '\0';
+}  // extern "C"
+
+namespace {
+
+// ring_local with the workspace requirement given by the caller (`need` bytes when two or more blocks are live).
+int ring_local_run(const void* q_shard, const attn_kv_block* kv_blocks, int n_blocks, void* o, float* lse, int B,
+                   int H, int Nq, int d, float scale, int causal, int64_t q_off, int pos_stride, int in_dtype,
+                   int o_dtype, void* workspace, size_t workspace_bytes, size_t need, void* stream) {
   int rc = check_query_side(q_shard, o, lse, B, H, Nq, d, scale, causal, q_off, pos_stride, in_dtype, o_dtype);
   if (rc != ATTN_OK) return rc;
   if (n_blocks < 0) return fail(ATTN_EINVAL, "negative n_blocks");
@@ -424,7 +428,6 @@ int ring_local(const void* q_shard, const attn_kv_block* kv_blocks, int n_blocks
 
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (live >= 2) {
-    const size_t need = ring_local_workspace_bytes(B, H, Nq, d);
     if (!workspace || workspace_bytes < need)
       return fail(ATTN_EWORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
                   workspace ? workspace_bytes : (size_t)0);
@@ -504,6 +507,18 @@ int ring_local(const void* q_shard, const attn_kv_block* kv_blocks, int n_blocks
   return ATTN_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+int ring_local(const void* q_shard, const attn_kv_block* kv_blocks, int n_blocks, void* o, float* lse, int B, int H,
+               int Nq, int d, float scale, int causal, int64_t q_off, int pos_stride, int in_dtype, int o_dtype,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = '\0';
+  return ring_local_run(q_shard, kv_blocks, n_blocks, o, lse, B, H, Nq, d, scale, causal, q_off, pos_stride,
+                        in_dtype, o_dtype, workspace, workspace_bytes, ring_local_workspace_bytes(B, H, Nq, d), stream);
+}
+
 size_t ring_local_pipelined_workspace_bytes(int B, int H, int Nq, int d, int Nk_max) {
   if (B < 0 || H < 0 || Nq < 0 || d < 0 || Nk_max < 0) return 0;
   const size_t rows = (size_t)B * H * Nq, kv = (size_t)B * H * Nk_max * d * 2;
@@ -575,9 +590,11 @@ int ring_local_pipelined(const void* q_shard, const attn_kv_block* kv_blocks, in
 
   // Two receive slots: while the compute stream attends the block in one slot, the copy stream brings the next
   // incoming block into the other. ready[s]: slot s holds its block; freed[s]: the compute that read slot s is
-  // done, so the slot may be overwritten.
-  hipEvent_t ready[2] = {nullptr, nullptr}, freed[2] = {nullptr, nullptr};
-  hipError_t e = hipSuccess;
+  // done, so the slot may be overwritten. entry: everything enqueued on the compute stream before this call --
+  // the producer of an incoming device block, an earlier call still reading the same workspace -- is done; the
+  // copy stream waits for it before its first copy.
+  hipEvent_t ready[2] = {nullptr, nullptr}, freed[2] = {nullptr, nullptr}, entry = nullptr;
+  hipError_t e = hipEventCreateWithFlags(&entry, hipEventDisableTiming);
   for (int s = 0; s < 2 && e == hipSuccess; ++s) {
     e = hipEventCreateWithFlags(&ready[s], hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&freed[s], hipEventDisableTiming);
@@ -587,6 +604,7 @@ int ring_local_pipelined(const void* q_shard, const attn_kv_block* kv_blocks, in
       if (ready[s]) (void)hipEventDestroy(ready[s]);
       if (freed[s]) (void)hipEventDestroy(freed[s]);
     }
+    if (entry) (void)hipEventDestroy(entry);
   };
   if (e != hipSuccess) {
     release();
@@ -622,7 +640,11 @@ int ring_local_pipelined(const void* q_shard, const attn_kv_block* kv_blocks, in
     ++done;
     return r;
   };
-  if (n_inc > 0) e = copy_in(0);
+  if (n_inc > 0) {
+    e = hipEventRecord(entry, cs);
+    if (e == hipSuccess) e = hipStreamWaitEvent(xs, entry, 0);
+    if (e == hipSuccess) e = copy_in(0);
+  }
   if (e == hipSuccess && n_blocks > 0 &&
       classify(Nq, kv_blocks[0].Nk, causal, q_off, kv_blocks[0].k_off, pos_stride) != 0) {
     rc = attend(kv_blocks[0].k, kv_blocks[0].v, kv_blocks[0]);

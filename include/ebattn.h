@@ -190,13 +190,17 @@ size_t ring_local_workspace_bytes(int B, int H, int Nq, int d);
  * has been attended. Incoming blocks may live in any memory hipMemcpyAsync reads (pinned host memory stands in
  * for the link to the neighbouring device, device memory for a block already received).
  *   Inputs      bf16 only (in_dtype is ATTN_BF16); blocks that hide every key are neither copied nor attended.
- *   Streams     compute_stream receives the attention launches and, at the end, holds the result; every copy
- *               is waited for by a launch on compute_stream, so synchronising compute_stream is enough.
+ *   Streams     compute_stream receives the attention launches and, at the end, holds the result. The first
+ *               copy waits for everything enqueued on compute_stream before the call (an incoming block produced
+ *               there, an earlier call still reading the same workspace); every copy is waited for by a launch on
+ *               compute_stream, so synchronising compute_stream is enough.
  *               Both are hipStream_t (NULL = the default stream), both of default priority, both on the
  *               current device (the call creates its ordering events there).
  *   workspace   at least ring_local_pipelined_workspace_bytes(B, H, Nq, d, Nk_max) bytes (Nk_max = the largest
  *               incoming block), 256-byte aligned, overlapping nothing else; it must stay untouched until
  *               compute_stream has passed this call's work. May be NULL only when block 0 is the only live one.
+ *   Host blocks incoming blocks in host memory are read by the copy engines after the call returns: they must
+ *               stay allocated and unchanged until compute_stream has passed this call's work.
  *   Errors      as ring_local; ATTN_EINVAL for more than ATTN_MAX_RING_BLOCKS live incoming blocks.
  *   The result equals ring_local over the same blocks. */
 int ring_local_pipelined(const void* q_shard, const attn_kv_block* kv_blocks, int n_blocks, void* o, float* lse,

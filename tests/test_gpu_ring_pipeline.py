@@ -103,3 +103,41 @@ def test_pipelined_ring_edge_blocks(eb):
     o, lse = eb.ring_local_pipelined(qd, [(kd, vd, 10 * n), (_host_bf16(k), _host_bf16(v), 20 * n)], causal=True)
     t.cuda.synchronize()
     assert bool((o == 0).all()) and bool(t.isneginf(lse).all())
+
+
+def test_pipelined_ring_back_to_back_on_one_workspace(eb):
+    """Calls in a row on ONE workspace, different blocks every call, no synchronisation between them:
+    * the first incoming block is a device tensor produced on the current stream just before the call, behind a
+      long attention launch (the copy stream must wait for it);
+    * the next call's copies must not overwrite receive slots the previous call's kernels still read;
+    * the host blocks are dropped right after each call and fresh pinned buffers of other values are allocated
+      (the binding keeps the dropped ones alive until the compute stream has passed the call).
+    Every result must equal ring_local over the same blocks, bit for bit."""
+    t = torch()
+    P, r, n, H, d = 4, 3, 2048, 8, 128         # rank 3 of 4: every block live, three incoming
+    dev = t.device("cuda:0")
+    ws = t.empty(eb.ring_local_pipelined_workspace_bytes(1, H, n, d, n), dtype=t.uint8, device=dev)
+    busy = [dev_bf16(normal_bf16_bits(70, x, (1, 32, 8192, 128))) for x in "qkv"]
+    scale = 1 / math.sqrt(d)
+    runs = []
+    for it in range(4):
+        print(f"[case] pipelined ring back to back, call {it}", flush=True)
+        seed = 71 + it
+        Q, K, V = (normal_bf16_bits(seed, x, (1, H, P * n, d)) for x in "qkv")
+        blk = lambda X, s: np.ascontiguousarray(X[:, :, s * n:(s + 1) * n])    # noqa: E731
+        qd = dev_bf16(blk(Q, r))
+        order = [(r - i) % P for i in range(P)]
+        ref_blocks = [(dev_bf16(blk(K, s)), dev_bf16(blk(V, s)), s * n) for s in order]
+        eb.attn_fwd(*busy, causal=False)                                   # a long kernel on the current stream
+        k_in, v_in = ref_blocks[1][0] * 1, ref_blocks[1][1] * 1            # produced behind it, same stream
+        pipe = [ref_blocks[0], (k_in, v_in, ref_blocks[1][2])]
+        pipe += [(_host_bf16(blk(K, s)), _host_bf16(blk(V, s)), s * n) for s in order[2:]]
+        o, lse = eb.ring_local_pipelined(qd, pipe, scale=scale, causal=True, q_off=r * n, workspace=ws)
+        del pipe, k_in, v_in
+        junk = [t.full((1, H, n, d), float(it + 2), dtype=t.bfloat16).pin_memory() for _ in range(4)]
+        runs.append((qd, ref_blocks, o, lse, junk))
+    t.cuda.synchronize()
+    for it, (qd, ref_blocks, o, lse, _) in enumerate(runs):
+        o1, l1 = eb.ring_local(qd, ref_blocks, scale=scale, causal=True, q_off=r * n)
+        t.cuda.synchronize()
+        assert t.equal(o1, o) and t.equal(l1, lse), f"call {it}: pipelined result differs from ring_local"

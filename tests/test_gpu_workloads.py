@@ -248,3 +248,72 @@ def test_causal_long_single_call_sampled(eb, key):
     oh, lh = host_f64(o), host_f64(lse)
     compare(np.stack([oh[b, h, rows] for b, h in heads]), np.stack([lh[b, h, rows] for b, h in heads]), o_ref, l_ref,
             TOL_BF16, TOL_LSE, what=f"{key} single call")
+
+
+def _unfused_share(eb, qd, blocks, scale, q_off, stride):
+    """The share as a chain of library calls: attn_fwd of each K/V block (in ring order) into an fp32 partial,
+    each partial folded into the running fp32 result by attn_lse_merge (in place), the last merge writing bf16 o.
+    Fully hidden blocks run too: their partial is (0, -inf) rows, which the merge weighs zero."""
+    t = torch()
+    acc_o = acc_l = None
+    for i, (kb, vb, k_off) in enumerate(blocks):
+        po, pl = eb.attn_fwd(qd, kb, vb, scale=scale, causal=True, q_off=q_off, k_off=k_off, pos_stride=stride,
+                             out_dtype=t.float32)
+        if acc_o is None:
+            acc_o, acc_l = po, pl
+            continue
+        last = i == len(blocks) - 1
+        out = t.empty(qd.shape, dtype=t.bfloat16, device=qd.device) if last else acc_o
+        out_l = t.empty_like(acc_l) if last else acc_l
+        acc_o, acc_l = eb.attn_lse_merge(acc_o, acc_l, po, pl, out=out, lse_out=out_l)
+    return acc_o, acc_l
+
+
+def test_ring_rank2of4_128k_unfused_merge_sampled(eb):
+    """The ring share (rank 2 of 4, global N = 131072) composed as the workload states it: attn_fwd per K/V block
+    into fp32 partials, combined with attn_lse_merge, against the oracle's rows of global causal attention."""
+    t = torch()
+    c = CONFIGS["ring_rank2of4_128k"]
+    n = c.Nq
+    print("[case] ring_rank2of4_128k unfused: attn_fwd partials + attn_lse_merge", flush=True)
+    Q = normal_bf16_bits(c.seed, "q", (c.B, c.H, c.global_N, c.d))
+    K = normal_bf16_bits(c.seed, "k", (c.B, c.H, c.global_N, c.d))
+    V = normal_bf16_bits(c.seed, "v", (c.B, c.H, c.global_N, c.d))
+    qd = dev_bf16(np.ascontiguousarray(Q[:, :, c.q_off:c.q_off + n]))
+    blocks = [(dev_bf16(np.ascontiguousarray(K[:, :, s * n:(s + 1) * n])),
+               dev_bf16(np.ascontiguousarray(V[:, :, s * n:(s + 1) * n])), s * n) for s in (2, 1, 0, 3)]
+    o, lse = _unfused_share(eb, qd, blocks, c.scale, c.q_off, 1)
+    t.cuda.synchronize()
+    assert o.dtype == t.bfloat16
+    rng = np.random.default_rng(13)
+    heads = [(0, 0), (0, 21)]
+    local = sample_rows(n, 128, 96, rng)
+    o_ref, l_ref = _oracle_rows(Q, K, V, heads, local + c.q_off, c.scale, causal=True)
+    oh, lh = host_f64(o), host_f64(lse)
+    compare(np.stack([oh[b, h, local] for b, h in heads]), np.stack([lh[b, h, local] for b, h in heads]), o_ref,
+            l_ref, TOL_BF16, TOL_LSE, what="ring rank 2 of 4 unfused (attn_fwd + attn_lse_merge)")
+
+
+@pytest.mark.parametrize("r", [1, 2])
+def test_striped_64k_unfused_merge_sampled(eb, r):
+    """A stripe of the striped workload (N = 65536, H = 16, stride 4) composed as attn_fwd per K/V stripe into
+    fp32 partials plus attn_lse_merge; stripe 1's row 0 sees only stripes 0 and 1, so its partials of stripes 2
+    and 3 are empty rows."""
+    t = torch()
+    c = CONFIGS[f"striped_r{r}_64k"]
+    W = 4
+    print(f"[case] striped r={r} unfused: attn_fwd partials + attn_lse_merge", flush=True)
+    Q = normal_bf16_bits(c.seed, "q", (c.B, c.H, c.global_N, c.d))
+    K = normal_bf16_bits(c.seed, "k", (c.B, c.H, c.global_N, c.d))
+    V = normal_bf16_bits(c.seed, "v", (c.B, c.H, c.global_N, c.d))
+    blocks = [(dev_bf16(np.ascontiguousarray(K[:, :, s::W])), dev_bf16(np.ascontiguousarray(V[:, :, s::W])), s)
+              for s in [(r - i) % W for i in range(W)]]
+    o, lse = _unfused_share(eb, dev_bf16(np.ascontiguousarray(Q[:, :, r::W])), blocks, c.scale, r, W)
+    t.cuda.synchronize()
+    rng = np.random.default_rng(14 + r)
+    heads = [(0, 0), (0, 9)]
+    local = sample_rows(c.Nq, 128, 64, rng)
+    o_ref, l_ref = _oracle_rows(Q, K, V, heads, local * W + r, c.scale, causal=True)
+    oh, lh = host_f64(o), host_f64(lse)
+    compare(np.stack([oh[b, h, local] for b, h in heads]), np.stack([lh[b, h, local] for b, h in heads]), o_ref,
+            l_ref, TOL_BF16, TOL_LSE, what=f"striped r={r} unfused (attn_fwd + attn_lse_merge)")
