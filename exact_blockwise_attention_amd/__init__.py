@@ -75,6 +75,8 @@ def _load() -> ctypes.CDLL:
     lib.attn_lse_merge.restype = I
     lib.ring_local.argtypes = [P, ctypes.POINTER(KVBlock), I, P, P, I, I, I, I, F, I, I64, I, I, I, P, SZ, P]
     lib.ring_local.restype = I
+    lib.ring_local_noalloc.argtypes = [P, ctypes.POINTER(KVBlock), I, P, P, I, I, I, I, F, I, I64, I, I, I, P]
+    lib.ring_local_noalloc.restype = I
     lib.ring_local_workspace_bytes.argtypes = [I, I, I, I]
     lib.ring_local_workspace_bytes.restype = SZ
     lib.ring_local_pipelined.argtypes = [P, ctypes.POINTER(KVBlock), I, P, P, I, I, I, I, F, I, I64, I, I, P, SZ, P, P]
@@ -413,6 +415,38 @@ _inflight_host_blocks: List[Tuple[object, List[object]]] = []
 
 def _retire_host_blocks() -> None:
     _inflight_host_blocks[:] = [(ev, ts) for ev, ts in _inflight_host_blocks if not ev.query()]
+
+
+# ATTN_NOALLOC_SCRATCH_BYTES of include/ebattn.h: the per-GPU scratch array behind ring_local_noalloc
+NOALLOC_SCRATCH_BYTES = 256 << 20
+
+
+def ring_local_noalloc(q_shard, kv_blocks, *, scale: Optional[float] = None, causal: bool = False, q_off: int = 0,
+                       pos_stride: int = 1, out=None, lse=None) -> Tuple[object, object]:
+    """ring_local without a caller workspace: the library's per-GPU scratch array holds the accumulator, and the
+    call allocates no device memory when `out` and `lse` are given (a share needs at most NOALLOC_SCRATCH_BYTES of
+    scratch). Calls whose work overlaps on one GPU race on that array; calls on one stream are ordered."""
+    torch = _torch()
+    _need_cuda(q_shard, out, lse)
+    for k, v, _ in kv_blocks:
+        _need_cuda(q_shard, k, v)
+        if k.dtype != q_shard.dtype or v.dtype != q_shard.dtype:
+            raise TypeError("blocks must share the query dtype")
+        if k.shape[:2] != q_shard.shape[:2] or k.shape != v.shape or k.shape[3] != q_shard.shape[3]:
+            raise ValueError("each block is k, v [B, H, Nk, d] with the query's B, H, d")
+    B, H, Nq, d = q_shard.shape
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=q_shard.dtype, device=q_shard.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q_shard.device)
+    arr, n = _blocks(kv_blocks)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _dims(B=B, H=H, Nq=Nq, d=d)
+    with torch.cuda.device(q_shard.device):   # the scratch array is looked up on the current device
+        _check(lib.ring_local_noalloc(_ptr(q_shard), arr, n, _ptr(out), _ptr(lse), B, H, Nq, d, scale, int(causal),
+                                      _arg("q_off", q_off, 64), _arg("pos_stride", pos_stride), _code(q_shard.dtype),
+                                      _code(out.dtype), _stream(q_shard)))
+    return out, lse
 
 
 def ring_local_pipelined_workspace_bytes(B: int, H: int, Nq: int, d: int, Nk_max: int) -> int:

@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/ebattn.h"
 #include "internal.h"
 
@@ -398,6 +400,14 @@ int ring_local_plan(const attn_kv_block* kv_blocks, int n_blocks, int Nq, int ca
 
 namespace {
 
+// Workspace ring_local actually touches: the fp32 accumulator (o, lse), plus the fp32 partial for fp32 inputs
+// (bf16 inputs merge in the attention epilogue and need no partial).
+size_t ring_local_bytes_used(int B, int H, int Nq, int d, int in_dtype) {
+  const size_t rows = (size_t)B * H * Nq;
+  const size_t one = align256(rows * d * 4) + align256(rows * 4);
+  return in_dtype == ATTN_F32 ? 2 * one : one;
+}
+
 // ring_local with the workspace requirement given by the caller (`need` bytes when two or more blocks are live).
 int ring_local_run(const void* q_shard, const attn_kv_block* kv_blocks, int n_blocks, void* o, float* lse, int B,
                    int H, int Nq, int d, float scale, int causal, int64_t q_off, int pos_stride, int in_dtype,
@@ -507,6 +517,34 @@ int ring_local_run(const void* q_shard, const attn_kv_block* kv_blocks, int n_bl
   return ATTN_OK;
 }
 
+// The no-allocation variant's scratch: one array per GPU, in the code object's device memory, that holds the fp32
+// accumulator (and, for fp32 inputs, the partial) of ring_local_noalloc. Host code never passes `scratch` itself
+// to a kernel or a copy (on the host it names a stand-in, not device memory): it uses the device address that
+// hipGetSymbolAddress returns for the current device, looked up once per device.
+static __device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch array (looked up on first use), or an error code.
+int scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(ATTN_EUNSUPPORTED, "device index %d above %d", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(ATTN_EHIP, "hipGetSymbolAddress(scratch) returned a null address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -517,6 +555,22 @@ int ring_local(const void* q_shard, const attn_kv_block* kv_blocks, int n_blocks
   g_err[0] = '\0';
   return ring_local_run(q_shard, kv_blocks, n_blocks, o, lse, B, H, Nq, d, scale, causal, q_off, pos_stride,
                         in_dtype, o_dtype, workspace, workspace_bytes, ring_local_workspace_bytes(B, H, Nq, d), stream);
+}
+
+int ring_local_noalloc(const void* q_shard, const attn_kv_block* kv_blocks, int n_blocks, void* o, float* lse, int B,
+                       int H, int Nq, int d, float scale, int causal, int64_t q_off, int pos_stride, int in_dtype,
+                       int o_dtype, void* stream) {
+  g_err[0] = '\0';
+  if (B < 0 || H < 0 || Nq < 0 || d < 0) return fail(ATTN_EINVAL, "negative size (B=%d H=%d Nq=%d d=%d)", B, H, Nq, d);
+  const size_t need = ring_local_bytes_used(B, H, Nq, d, in_dtype);
+  if (need > (size_t)ATTN_NOALLOC_SCRATCH_BYTES)
+    return fail(ATTN_EWORKSPACE, "ring_local_noalloc: this share needs %zu bytes of scratch, above the %zu-byte array",
+                need, (size_t)ATTN_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  int rc = scratch_ptr(&ws);
+  if (rc != ATTN_OK) return rc;
+  return ring_local_run(q_shard, kv_blocks, n_blocks, o, lse, B, H, Nq, d, scale, causal, q_off, pos_stride, in_dtype,
+                        o_dtype, ws, (size_t)ATTN_NOALLOC_SCRATCH_BYTES, need, stream);
 }
 
 size_t ring_local_pipelined_workspace_bytes(int B, int H, int Nq, int d, int Nk_max) {

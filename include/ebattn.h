@@ -180,6 +180,29 @@ int ring_local(const void* q_shard, const attn_kv_block* kv_blocks, int n_blocks
  * second is used with fp32 inputs only). Returns 0 for negative sizes. */
 size_t ring_local_workspace_bytes(int B, int H, int Nq, int d);
 
+/* Size of the per-GPU scratch array behind ring_local_noalloc: 256 MiB, enough for the fp32 accumulator of a
+ * share of up to about 500 thousand query rows (B*H*Nq) at d = 128 with bf16 inputs, half that with fp32 inputs. */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+
+/* ring_local_noalloc -- ring_local for callers that cannot allocate memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same computation, kernels and results as ring_local, with
+ * the workspace taken from a scratch array that the library holds in each GPU's memory (ATTN_NOALLOC_SCRATCH_BYTES,
+ * reserved on a GPU while its code object is loaded, until the process ends) instead of a caller's buffer. The
+ * call allocates nothing: no hipMalloc, no hipFree, no library routine that allocates. Its first call on a device
+ * looks the array's device address up on the current device, which must be the device of q_shard, o, lse, the
+ * blocks and `stream`.
+ *   Scratch     a share needs B*H*Nq*(d + 1)*4 bytes (each part rounded up to 256 bytes), twice that with fp32
+ *               inputs; more than ATTN_NOALLOC_SCRATCH_BYTES returns ATTN_EWORKSPACE before anything is launched.
+ *               Nothing in the array needs to start at any value: every call writes its accumulator before reading
+ *               it, and the array keeps the last call's contents.
+ *   Concurrency every call on one GPU uses that GPU's single array: calls whose work overlaps on the device (on
+ *               different streams, or from different threads without ordering) race and give wrong results. Calls
+ *               enqueued on one stream are ordered and safe.
+ *   Arguments, masks, dtypes and errors otherwise as ring_local. */
+int ring_local_noalloc(const void* q_shard, const attn_kv_block* kv_blocks, int n_blocks, void* o, float* lse,
+                       int B, int H, int Nq, int d, float scale, int causal, int64_t q_off, int pos_stride,
+                       int in_dtype, int o_dtype, void* stream);
+
 /* ring_local_pipelined -- ring_local with the exchange step of the ring on the same device: compute on the block
  * in hand while the next one arrives ("架构层解决方案 - Sparse Attention与Ring Attention", Ring Attention /
  * 计算-通信重叠; "Mosaic多轴注意力分片：突破Transformer长序列处理瓶颈" §3.2). kv_blocks[0] is this device's own
