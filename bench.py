@@ -39,7 +39,7 @@ METRIC = "attention fwd TFLOP/s + % bf16 MFMA peak (causal, N=8K..128K, 1 GPU)"
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk/CU
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 KERNEL_SOURCE = os.path.join(ROOT, "exact_blockwise_attention_amd", "csrc", "attn_fwd_mfma.hip")
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "attn_fwd_causal_8k_hbm_traffic.txt")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "attn_fwd_causal_8k.txt")
 
 
 def kernel_hash() -> str:
@@ -130,6 +130,95 @@ def cpu_baseline_single_thread(cfg, q_bits, k_bits, v_bits):
     fl = acc.attention_flops(acc.visible_pairs(cfg.Nq, cfg.Nk_total, cfg.causal), cfg.d)
     return {"value": fl / el / 1e12, "unit": "TFLOP/s", "cores": 1, "seconds": el,
             "sample": f"1 (batch, head) slice of {cfg.key}, all {cfg.Nq} query rows"}
+
+
+def _oracle_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([p.get("num_threads", 1) for p in threadpool_info()] or [1]))
+    except Exception:
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline_other_configs(rows_per_head=64, heads=2):
+    """The float64 oracle, as it stands, on the other workloads: the tiny fp32 one in full (unsplit, and split into
+    four key blocks merged by the oracle's merge), and the ring share, a stripe and both tabular axes on a seeded
+    sample (rows_per_head query rows of `heads` (batch, head) slices against their full key sets; feature axis:
+    2000 (row, head) slices). Sampled timings are extrapolated linearly in visible (query, key) pairs to the full
+    workload and say so; rates count 4*d FLOP per visible pair, as the GPU figures do."""
+    import numpy as np
+    import oracle
+    from workloads import CONFIGS, bf16_bits_to_f64, normal_bf16_slab, normal_f32
+    from workloads import accounting as acc
+    cores = _oracle_threads()
+    out = {}
+    # tiny fp32, full tensors
+    c1 = CONFIGS["tiny_f32"]
+    q, k, v = (normal_f32(c1.seed, x, (c1.B, c1.H, c1.Nq, c1.d)) for x in "qkv")
+    t0 = time.perf_counter()
+    oracle.attention(q, k, v, c1.scale)
+    t_full = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    parts = [oracle.attention(q, k[:, :, j:j + n], v[:, :, j:j + n], c1.scale) for n, j in c1.blocks]
+    oracle.lse_merge_many(parts)
+    t_split = time.perf_counter() - t0
+    fl = acc.attention_flops(acc.config_pairs(c1), c1.d)
+    out["tiny_f32"] = {"seconds_unsplit": t_full, "seconds_split_and_merged": t_split,
+                       "GFLOP/s": fl / t_full / 1e9, "cores": cores, "extrapolated": False,
+                       "sample": "full tensors, unsplit and as four key blocks merged"}
+    rng = np.random.default_rng(12345)
+
+    def sampled(key, cfg, kv_slab, q_rows_global, kv_len, q_pos0, stride, causal, scale, full_pairs):
+        """q_rows_global: the sampled rows' indices in the global query sequence."""
+        t = 0.0
+        pairs = 0
+        for b, h in [(0, hh) for hh in range(heads)]:
+            qs = normal_bf16_slab(cfg.seed, "q", b, h, (cfg.global_N if cfg.global_N else cfg.Nq, cfg.d))
+            kk = normal_bf16_slab(cfg.seed, "k", b, h, (kv_len, cfg.d))
+            vv = normal_bf16_slab(cfg.seed, "v", b, h, (kv_len, cfg.d))
+            qf = bf16_bits_to_f64(qs)[None, None]
+            kf, vf = bf16_bits_to_f64(kv_slab(kk))[None, None], bf16_bits_to_f64(kv_slab(vv))[None, None]
+            t0 = time.perf_counter()
+            oracle.attention(qf, kf, vf, scale, causal=causal, q_off=q_pos0, stride=stride, rows=q_rows_global)
+            t += time.perf_counter() - t0
+            nk = kf.shape[2]
+            pairs += sum(acc.visible_pairs(1, nk, causal, q_pos0 + stride * int(r), 0, stride) for r in q_rows_global)
+        fl_sample = acc.attention_flops(pairs, cfg.d)
+        return {"seconds_sample": t, "GFLOP/s": fl_sample / t / 1e9, "cores": cores, "extrapolated": True,
+                "seconds_full_extrapolated": t * full_pairs / pairs,
+                "sample": f"{len(q_rows_global)} query rows of each of {heads} (batch, head) slices against "
+                          f"their full key set ({pairs} visible pairs); full = {full_pairs} pairs"}
+
+    # ring share, rank 2 of 4: the shard's rows are global rows q_off.., keys are the whole global sequence
+    c3 = CONFIGS["ring_rank2of4_128k"]
+    r3 = np.sort(rng.choice(c3.Nq, rows_per_head, replace=False)) + c3.q_off
+    out["ring_rank2of4_128k"] = sampled("c3", c3, lambda x: x, r3, c3.global_N, 0, 1, True, c3.scale,
+                                        acc.config_pairs(c3))
+    # striped, stripe 1: local row i is global position 4i+1; keys are the whole global sequence
+    c4 = CONFIGS["striped_r1_64k"]
+    r4 = 4 * np.sort(rng.choice(c4.Nq, rows_per_head, replace=False)) + 1
+    out["striped_r1_64k"] = sampled("c4", c4, lambda x: x, r4, c4.global_N, 0, 1, True, c4.scale,
+                                    acc.config_pairs(c4))
+    # tabular row axis (non-causal, 150000 keys)
+    c5 = CONFIGS["tabular_rows_150k"]
+    r5 = np.sort(rng.choice(c5.Nq, rows_per_head, replace=False))
+    out["tabular_rows_150k"] = sampled("c5", c5, lambda x: x, r5, c5.Nq, 0, 1, False, c5.scale,
+                                       acc.config_pairs(c5))
+    # tabular feature axis: 2000 of the 600000 (row, head) slices of 8 tokens, in full
+    cf = CONFIGS["tabular_features_8"]
+    nsl = 2000
+    qf = np.stack([bf16_bits_to_f64(normal_bf16_slab(cf.seed, "q", i, 0, (cf.Nq, cf.d))) for i in range(nsl)])
+    kf = np.stack([bf16_bits_to_f64(normal_bf16_slab(cf.seed, "k", i, 0, (cf.Nq, cf.d))) for i in range(nsl)])
+    vf = np.stack([bf16_bits_to_f64(normal_bf16_slab(cf.seed, "v", i, 0, (cf.Nq, cf.d))) for i in range(nsl)])
+    t0 = time.perf_counter()
+    oracle.attention(qf[:, None], kf[:, None], vf[:, None], cf.scale)
+    t = time.perf_counter() - t0
+    total = cf.B * cf.H
+    out["tabular_features_8"] = {"seconds_sample": t, "cores": cores, "extrapolated": True,
+                                 "GFLOP/s": acc.attention_flops(nsl * cf.Nq * cf.Nq, cf.d) / t / 1e9,
+                                 "seconds_full_extrapolated": t * total / nsl,
+                                 "sample": f"{nsl} of the {total} (row, head) slices of 8 tokens, in full"}
+    return out
 
 
 def bench_merge(torch, eb, dev, steps):
@@ -481,6 +570,10 @@ def clock_power_under_load(torch, fn, seconds=3.0):
 # rocprofv3: GRBM_GUI_ACTIVE over its 8 XCDs (cycles the GPU was busy, per XCD, once divided), the SQ cycle
 # counters over the 1024 SIMDs.
 N_XCD, N_SIMD = 8, 1024
+# v_exp_f32 issue rate measured on this part: a chain of exponentials takes 3.65 times as long as the same chain of
+# fp32 FMAs, which issue at 128 lanes per clock per CU (4 SIMDs x 32 lanes), so about 35 lanes per clock per CU;
+# the figure used is a quarter of the FMA rate
+EXP_LANES_PER_CLK_CU = 32
 SQ_COUNTERS = ["SQ_WAVES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA",
                "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_LDS", "SQ_WAIT_INST_LDS", "GRBM_GUI_ACTIVE"]
 # second pass: executed bf16 MFMA work (512 FLOP per counted op), transcendental instructions (one per lane per
@@ -569,7 +662,8 @@ def derive_sq(c, c2, kernel_ns):
         out["mfma_flop_executed"] = c2["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
         out["mfma_tflops_executed"] = out["mfma_flop_executed"] / kernel_ns / 1e3
         out["exp_lane_ops"] = c2["SQ_INSTS_VALU_TRANS_F32"] * 64
-        out["valu_active_per_simd_cycle"] = c2["SQ_ACTIVE_INST_VALU"] / N_SIMD / (c2["GRBM_GUI_ACTIVE"] / N_XCD)
+        # SQ_ACTIVE_INST_VALU counts quad-cycles (4 clocks) summed over the SIMDs
+        out["valu_busy"] = 4 * c2["SQ_ACTIVE_INST_VALU"] / N_SIMD / (c2["GRBM_GUI_ACTIVE"] / N_XCD)
     return out
 
 
@@ -577,6 +671,7 @@ def profile_kind(kind, outdir, traffic=False, limit_s=240):
     """Kernel trace, SQ counters and (with traffic) the FETCH_SIZE / WRITE_SIZE passes of one step kind. Returns
     {"commands": [...], kernel substring: {figures}} or {"error": ...}."""
     _, kernels, steps, warmup = PROFILE_TARGETS[kind]
+    outdir = os.path.abspath(outdir)          # the child runs with the temporary directory as its cwd
     res = {"commands": []}
     cmd, rc = _rocprof_child(kind, ["--kernel-trace", "--stats"], os.path.join(outdir, "trace"), steps, warmup,
                              limit_s=limit_s)
@@ -625,6 +720,96 @@ def profile_kind(kind, outdir, traffic=False, limit_s=240):
     return res
 
 
+PROFILE_SUMMARY = {
+    # kind -> (title, kernel source, (kernel substring, label, flop, algorithmic bytes) per kernel)
+    "fwd": "attention forward, causal self-attention B=4 H=32 N=8192 d=128 (bf16 q, k, v, o; fp32 lse)",
+    "bwd": "attention backward, causal self-attention B=4 H=32 N=8192 d=128 (bf16 q, k, v, dout; fp32 dq, dk, dv)",
+    "merge": "LSE merge of two fp32 partials in place, 1,048,576 rows x d=128 (the ring-share shape)",
+    "rows": "tabular row axis, 8 x 4 sequences of 150000 tokens, d=24, non-causal (bf16 in and out)",
+}
+SOURCES = {"fwd": "attn_fwd_mfma.hip", "bwd": "attn_bwd_mfma.hip", "merge": "lse_merge.hip", "rows": "attn_fwd_mfma.hip"}
+
+
+def source_hash(name):
+    with open(os.path.join(ROOT, "exact_blockwise_attention_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def profile_accounting(kind):
+    """(kernel substring -> algorithmic FLOP per launch or None, algorithmic HBM bytes per launch) of a kind."""
+    from workloads import CONFIGS
+    from workloads import accounting as acc
+    if kind == "fwd":
+        c = CONFIGS["causal_8k"]
+        return ({"attn_fwd_kernel<128": acc.attention_flops(acc.config_pairs(c), c.d)},
+                acc.attn_fwd_bytes(c.B, c.H, c.Nq, c.Nq, c.d, 2, 2))
+    if kind == "rows":
+        c = CONFIGS["tabular_rows_150k"]
+        return ({"attn_fwd_kernel<24": acc.attention_flops(acc.config_pairs(c), c.d)},
+                acc.attn_fwd_bytes(c.B, c.H, c.Nq, c.Nq, c.d, 2, 2))
+    if kind == "bwd":
+        B, H, N, d = 4, 32, 8192, 128
+        pairs = B * H * acc.visible_pairs(N, N, True)
+        # dq kernel: S, dP recomputed and dQ (three products); dk/dv kernel: S, dP, dV, dK (four)
+        return ({"attn_bwd_dq_kernel<128": 3 * 2 * d * pairs, "attn_bwd_dkdv_kernel<128": 4 * 2 * d * pairs},
+                B * H * N * (5 * d * 2 + 4 + 3 * d * 4 + 4))
+    if kind == "merge":
+        return ({"lse_merge_kernel": None}, acc.merge_bytes(32 * 32768, 128, 4, 4))
+    raise ValueError(kind)
+
+
+def write_profile_summary(kind, res, path):
+    flops, alg_bytes = profile_accounting(kind)
+    lines = [f"# rocprofv3 summary: {PROFILE_SUMMARY[kind]}",
+             f"made by: python bench.py --profile {kind} --profile-out <dir> --profile-summary {os.path.relpath(path, ROOT)}",
+             "which runs, each in a child process under its own time limit (cwd and TMPDIR = /tmp):"]
+    lines += [f"  {c}" for c in res.get("commands", [])]
+    lines.append(f"kernel_source_sha256_16: {source_hash(SOURCES[kind])}")
+    lines.append(f"bf16 dense MFMA peak used: {PEAK_BF16_TFLOPS} TFLOP/s (256 CU x 2.4 GHz x 4096 FLOP/clk); "
+                 f"HBM peak {PEAK_HBM_GBS:.0f} GB/s")
+    for sub, fig in res.items():
+        if not isinstance(fig, dict) or sub == "commands":
+            continue
+        lines.append(f"kernel {sub}...:")
+        if "error" in fig:
+            lines.append(f"  error: {fig['error']}")
+            continue
+        ns = fig["kernel_ns_avg"]
+        lines.append(f"  timed dispatches (last {fig['dispatches_timed']}): avg_ns={ns:.0f} "
+                     f"median_ns={fig['kernel_ns_median']:.0f}")
+        fl = flops.get(sub)
+        if fl:
+            lines.append(f"  algorithmic FLOP per launch: {fl:.4e} -> {fl / ns / 1e3:.1f} TFLOP/s at the trace average "
+                         f"= {fl / ns / 1e3 / PEAK_BF16_TFLOPS:.4f} of peak")
+        lines.append(f"  MFMA busy per SIMD: {fig['mfma_busy']:.4f}; clock during the kernel {fig['clock_ghz']:.3f} GHz "
+                     f"(GRBM_GUI_ACTIVE per XCD / trace duration), bf16 peak at that clock "
+                     f"{PEAK_BF16_TFLOPS * fig['clock_ghz'] / 2.4:.1f} TFLOP/s")
+        if "mfma_tflops_executed" in fig:
+            lines.append(f"  MFMA FLOP executed per launch: {fig['mfma_flop_executed']:.4e} "
+                         f"(SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512) -> {fig['mfma_tflops_executed']:.1f} TFLOP/s")
+            lines.append(f"  transcendental lane-ops per launch: {fig['exp_lane_ops']:.4e} (SQ_INSTS_VALU_TRANS_F32 x 64) "
+                         f"-> {fig['exp_lane_ops'] / ns:.4e} per ns = {fig['exp_lane_ops'] / ns / (256 * EXP_LANES_PER_CLK_CU * fig['clock_ghz']):.3f} "
+                         f"of the transcendental rate at that clock ({EXP_LANES_PER_CLK_CU} lanes/clk/CU)")
+            lines.append(f"  vector ALU busy per SIMD: {fig['valu_busy']:.3f} (4 x SQ_ACTIVE_INST_VALU quad-cycles / SIMD-cycles)")
+        lines.append(f"  VALU per MFMA {fig['valu_per_mfma']:.2f}; LDS instructions per MFMA {fig['lds_per_mfma']:.2f}; "
+                     f"LDS wait per wave-cycle {fig['lds_wait_per_wave_cycle']:.4f}")
+        if "fetch_size_bytes" in fig and "write_size_bytes" in fig:
+            tot = fig["fetch_size_bytes"] + fig["write_size_bytes"]
+            lines.append(f"  calibration: torch's plain device copy of 1073741824 bytes gives bytes per counted byte "
+                         f"fetch x{fig['fetch_size_scale']:.4f}, write x{fig['write_size_scale']:.4f}")
+            lines.append(f"  hbm_fetch_bytes_per_launch: {fig['fetch_size_bytes']:.4e}  "
+                         f"hbm_write_bytes_per_launch: {fig['write_size_bytes']:.4e}")
+            lines.append(f"  hbm_bytes_per_launch: {tot:.4e}")
+            lines.append(f"  algorithmic_bytes_per_launch: {alg_bytes:.4e} (inputs read once, outputs written once); "
+                         f"traffic / algorithmic: {tot / alg_bytes:.3f}")
+            if kind == "merge":
+                lines.append(f"  achieved: {alg_bytes / ns:.1f} GB/s = {alg_bytes / ns / PEAK_HBM_GBS:.3f} of "
+                             f"{PEAK_HBM_GBS:.0f} GB/s")
+        lines.append("  counters per dispatch: " + ", ".join(f"{k}={v:.4e}" for k, v in sorted(fig["counters"].items())))
+    with open(path, "w", encoding="utf-8") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -646,6 +831,8 @@ def main(argv=None):
                     help="only run the rocprofv3 passes (trace, SQ counters, HBM traffic) of one step kind into "
                          "--profile-out and print their figures as one JSON line")
     ap.add_argument("--profile-out", default=os.path.join(ROOT, "gpurun_out", "profile"))
+    ap.add_argument("--profile-summary", default=None,
+                    help="with --profile: also write the figures as a text summary to this path")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the library has no "
@@ -654,7 +841,9 @@ def main(argv=None):
 
     if args.profile:
         res = profile_kind(args.profile, os.path.join(args.profile_out, args.profile), traffic=True)
-        res["kernel_source_sha256_16"] = kernel_hash()
+        res["kernel_source_sha256_16"] = source_hash(SOURCES[args.profile])
+        if args.profile_summary and "error" not in res:
+            write_profile_summary(args.profile, res, os.path.abspath(args.profile_summary))
         print(json.dumps(res), flush=True)
         return 0 if "error" not in res else 1
 
@@ -753,7 +942,7 @@ def main(argv=None):
             rf["valu_per_mfma"] = round(fig["valu_per_mfma"], 3)
             if "mfma_tflops_executed" in fig:
                 rf["mfma_tflops_executed"] = round(fig["mfma_tflops_executed"], 1)
-                rf["valu_active_per_simd_cycle"] = round(fig["valu_active_per_simd_cycle"], 4)
+                rf["valu_busy"] = round(fig["valu_busy"], 4)
             rf["counters_from"] = ("rocprofv3 child passes on this GPU after the timed region: " +
                                    "; ".join(prof["commands"]))
         else:
@@ -772,6 +961,9 @@ def main(argv=None):
         result["cpu_baseline"] = cpu_baseline(cfg, q_bits, k_bits, v_bits)
         if "extra" in result and isinstance(result["extra"], dict):
             result["extra"]["cpu_oracle_single_thread"] = cpu_baseline_single_thread(cfg, q_bits, k_bits, v_bits)
+            t_o = time.perf_counter()
+            result["extra"]["cpu_oracle_other_workloads"] = cpu_baseline_other_configs()
+            log(f"[bench] oracle on the other workloads: {time.perf_counter() - t_o:.1f} s")
     print(json.dumps(result), flush=True)
     return 0
 

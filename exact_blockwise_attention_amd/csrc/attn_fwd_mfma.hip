@@ -348,12 +348,14 @@ __device__ __forceinline__ void pv_tile(const char* vt, const bf16x8 (&pb)[4], f
 //
 // Phase 1: the 16 MFMAs of the next tile's scores, beside the current tile's row maximum (slots 0-3), reference
 // update (slot 4), the weights of keys 0..31 (slots 5-12) and their bf16 rounding (slots 10, 14); the even slots
-// also issue this wave's share of the copies of K tile t+2 and V tile t+1.
+// also issue this wave's share of the copies of K tile t+2 and V tile t+1, and the last three slots, whose vector
+// work is light, read phase 2's first V^T operands (the V tile is resident since the stage's barrier), so that
+// phase 2 does not open with a wait on the LDS.
 template <int D, class CopyK, class CopyV>
 __device__ __forceinline__ void stage_phase1(const char* kn, const bf16x8 (&qf)[Geom<D>::KSTEPS], f32x16& n0,
                                              f32x16& n1, const LaneAddr<D>& la, float (&w)[32], bf16x8 (&pb)[4],
                                              float& m_ref, float& alpha, bool& need, float& m_use, float scale_log2,
-                                             const CopyK& ck, const CopyV& cv) {
+                                             const CopyK& ck, const CopyV& cv, const char* vc, bf16x8 (&vpre)[kLead]) {
   constexpr int NM = 2 * Geom<D>::KSTEPS;
   static_assert(NM == 16, "the slot plan below is laid out for 16 MFMAs per phase");
   static_assert(CopyK::kPerWave <= 4 && CopyV::kPerWave <= 4, "one tile-copy instruction per even slot");
@@ -399,23 +401,26 @@ __device__ __forceinline__ void stage_phase1(const char* kn, const bf16x8 (&qf)[
       pb[1] = pack_weights(w, 1);
       pin(pb[1]);
     }
+    if (i >= NM - kLead) vpre[i - (NM - kLead)] = v_frag<D>(vc, la, i - (NM - kLead));
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// Phase 2: the 16 MFMAs of P.V for the current tile, beside the weights of keys 32..63 (slots 0-7), their bf16
-// rounding (slots 5, 9; each needed three slots later) and both row sums (the bf16 one on the matrix unit in
-// slots 1, 5, 9, 13).
+// Phase 2: the 16 MFMAs of P.V for the current tile (its first V^T operands read in phase 1), beside the weights
+// of keys 32..63 (slots 0-7), their bf16 rounding (slots 5, 9; each needed three slots later) and both row sums
+// (the bf16 one on the matrix unit in slots 1, 5, 9, 13; the fp32 one in four partial sums, each started from
+// its first pair).
 template <int D>
 __device__ __forceinline__ void stage_phase2(const char* vc, f32x16 (&acc)[Geom<D>::CT], const LaneAddr<D>& la,
                                              float (&w)[32], bf16x8 (&pb)[4], float alpha, float m_use,
-                                             float scale_log2, float& l_run, const bf16x8& sel, f32x4& lq) {
+                                             float scale_log2, float& l_run, const bf16x8& sel, f32x4& lq,
+                                             const bf16x8 (&vpre)[kLead]) {
   using G = Geom<D>;
   constexpr int NM = 4 * G::CT;
   static_assert(NM == 16, "the slot plan below is laid out for 16 MFMAs per phase");
   bf16x8 vf[kLead + 1];
 #pragma unroll
-  for (int j = 0; j < kLead; ++j) vf[j] = v_frag<D>(vc, la, j);
+  for (int j = 0; j < kLead; ++j) vf[j] = vpre[j];
   float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int j = 0; j < NM; ++j) {
@@ -425,7 +430,10 @@ __device__ __forceinline__ void stage_phase2(const char* vc, f32x16 (&acc)[Geom<
       const int e = 16 + 2 * j;
       w[e] = weight(w[e], scale_log2, m_use);
       w[e + 1] = weight(w[e + 1], scale_log2, m_use);
-      p[j & 3] += w[2 * j] + w[2 * j + 1];
+      if (j < 4)
+        p[j] = w[2 * j] + w[2 * j + 1];
+      else
+        p[j & 3] += w[2 * j] + w[2 * j + 1];
     } else {
       p[j & 3] += w[2 * j] + w[2 * j + 1];
     }
@@ -693,11 +701,12 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
         // Raised wave priority for phase 1: its chain (row maximum -> reference -> weights) gates the next phase,
         // so the issue arbiter favours it over the SIMD's other wave (measured: +2.5 % causal, +0.7 % unmasked).
         __builtin_amdgcn_s_setprio(1);
-        stage_phase1<D>(kn, qf, n0, n1, la, w, pb, m_ref, alpha, need, m_use, a.scale_log2, ck, cv);
+        bf16x8 vpre[kLead];
+        stage_phase1<D>(kn, qf, n0, n1, la, w, pb, m_ref, alpha, need, m_use, a.scale_log2, ck, cv, vc, vpre);
         __builtin_amdgcn_s_setprio(0);
         rescale_acc<D>(acc, lq, alpha, need);
         __builtin_amdgcn_sched_barrier(0);
-        stage_phase2<D>(vc, acc, la, w, pb, alpha, m_use, a.scale_log2, l_run, rsel, lq);
+        stage_phase2<D>(vc, acc, la, w, pb, alpha, m_use, a.scale_log2, l_run, rsel, lq, vpre);
       };
       for (int t = t0; t < ntiles; t += 2) {
         stage(t, sa0, sa1, sb0, sb1, k1, k0, v0, v1);

@@ -30,6 +30,13 @@ def test_generation_is_seeded_and_per_head():
     assert abs(x.mean()) < 0.02 and abs(x.std() - 1) < 0.02
 
 
+def test_single_slab_draw_matches_the_full_tensor():
+    from workloads import normal_bf16_slab
+    full = normal_bf16_bits(11, "v", (2, 3, 40, 24))
+    for b, h in ((0, 0), (1, 2), (0, 1)):
+        assert np.array_equal(normal_bf16_slab(11, "v", b, h, (40, 24)), full[b, h])
+
+
 def test_mask_probe_values_exact_in_bf16():
     q, k, v = mask_probe_inputs(8, 64, 131000, 131000 - 70, 1)
     for a in (q, k, v):

@@ -9,6 +9,7 @@ from .inputs import (  # noqa: F401
     bf16_bits_to_f64,
     f32_to_bf16_bits,
     normal_bf16_bits,
+    normal_bf16_slab,
     normal_f32,
     mask_probe_inputs,
 )

@@ -93,6 +93,13 @@ def normal_bf16_bits(seed: int, tensor: str, shape, heads=None) -> np.ndarray:
     return out.reshape(x.shape)
 
 
+def normal_bf16_slab(seed: int, tensor: str, b: int, h: int, slab_shape) -> np.ndarray:
+    """The (b, h) slab of normal_bf16_bits(seed, tensor, (B, H, *slab_shape)) alone, drawn from the same seed
+    (uint16 bit patterns of shape slab_shape)."""
+    x = _slab_rng(seed, tensor, b, h).standard_normal(tuple(int(s) for s in slab_shape), dtype=np.float32)
+    return f32_to_bf16_bits(x)
+
+
 def mask_probe_inputs(nq: int, nk: int, q_off: int, k_off: int, stride: int, alpha: float = 512.0):
     """Constructed inputs whose attention output names the last visible key position.
 
