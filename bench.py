@@ -736,32 +736,38 @@ def source_hash(name):
 
 
 def profile_accounting(kind):
-    """(kernel substring -> algorithmic FLOP per launch or None, algorithmic HBM bytes per launch) of a kind."""
+    """Per kernel substring of a kind: (FLOP of the kernel's products per launch, 2*d per visible pair each, or
+    None; algorithmic HBM bytes per launch: each input read once, each output written once; what the FLOP count)."""
     from workloads import CONFIGS
     from workloads import accounting as acc
     if kind == "fwd":
         c = CONFIGS["causal_8k"]
-        return ({"attn_fwd_kernel<128": acc.attention_flops(acc.config_pairs(c), c.d)},
-                acc.attn_fwd_bytes(c.B, c.H, c.Nq, c.Nq, c.d, 2, 2))
+        return {"attn_fwd_kernel<128": (acc.attention_flops(acc.config_pairs(c), c.d),
+                                        acc.attn_fwd_bytes(c.B, c.H, c.Nq, c.Nq, c.d, 2, 2), "algorithmic")}
     if kind == "rows":
         c = CONFIGS["tabular_rows_150k"]
-        return ({"attn_fwd_kernel<24": acc.attention_flops(acc.config_pairs(c), c.d)},
-                acc.attn_fwd_bytes(c.B, c.H, c.Nq, c.Nq, c.d, 2, 2))
+        return {"attn_fwd_kernel<24": (acc.attention_flops(acc.config_pairs(c), c.d),
+                                       acc.attn_fwd_bytes(c.B, c.H, c.Nq, c.Nq, c.d, 2, 2), "algorithmic")}
     if kind == "bwd":
         B, H, N, d = 4, 32, 8192, 128
-        pairs = B * H * acc.visible_pairs(N, N, True)
-        # dq kernel: S, dP recomputed and dQ (three products); dk/dv kernel: S, dP, dV, dK (four)
-        return ({"attn_bwd_dq_kernel<128": 3 * 2 * d * pairs, "attn_bwd_dkdv_kernel<128": 4 * 2 * d * pairs},
-                B * H * N * (5 * d * 2 + 4 + 3 * d * 4 + 4))
+        pairs, rows = B * H * acc.visible_pairs(N, N, True), B * H * N
+        # dq kernel: S and dP recomputed, then dQ (three products); reads q, k, v, o, dout (bf16) and lse, writes
+        # dq (fp32) and delta. dk/dv kernel: S, dP, dV, dK (four products); reads q, k, v, dout, lse and delta,
+        # writes dk and dv (fp32). The algorithmic backward is five products: S, dP, dV, dQ, dK.
+        return {"attn_bwd_dq_kernel<128": (3 * 2 * d * pairs, rows * (5 * d * 2 + 4 + d * 4 + 4),
+                                           "three products, two of them the recomputation of S and dP"),
+                "attn_bwd_dkdv_kernel<128": (4 * 2 * d * pairs, rows * (4 * d * 2 + 8 + 2 * d * 4),
+                                             "four products")}
     if kind == "merge":
-        return ({"lse_merge_kernel": None}, acc.merge_bytes(32 * 32768, 128, 4, 4))
+        return {"lse_merge_kernel": (None, acc.merge_bytes(32 * 32768, 128, 4, 4), "")}
     raise ValueError(kind)
 
 
 def write_profile_summary(kind, res, path):
-    flops, alg_bytes = profile_accounting(kind)
+    accounting = profile_accounting(kind)
     lines = [f"# rocprofv3 summary: {PROFILE_SUMMARY[kind]}",
-             f"made by: python bench.py --profile {kind} --profile-out <dir> --profile-summary {os.path.relpath(path, ROOT)}",
+             f"made by: python bench.py --profile {kind} --profile-out <dir> --profile-summary "
+             f"profiles/{os.path.basename(path)}",
              "which runs, each in a child process under its own time limit (cwd and TMPDIR = /tmp):"]
     lines += [f"  {c}" for c in res.get("commands", [])]
     lines.append(f"kernel_source_sha256_16: {source_hash(SOURCES[kind])}")
@@ -777,22 +783,27 @@ def write_profile_summary(kind, res, path):
         ns = fig["kernel_ns_avg"]
         lines.append(f"  timed dispatches (last {fig['dispatches_timed']}): avg_ns={ns:.0f} "
                      f"median_ns={fig['kernel_ns_median']:.0f}")
-        fl = flops.get(sub)
+        fl, alg_bytes, what = accounting[sub]
         if fl:
-            lines.append(f"  algorithmic FLOP per launch: {fl:.4e} -> {fl / ns / 1e3:.1f} TFLOP/s at the trace average "
-                         f"= {fl / ns / 1e3 / PEAK_BF16_TFLOPS:.4f} of peak")
-        lines.append(f"  MFMA busy per SIMD: {fig['mfma_busy']:.4f}; clock during the kernel {fig['clock_ghz']:.3f} GHz "
-                     f"(GRBM_GUI_ACTIVE per XCD / trace duration), bf16 peak at that clock "
-                     f"{PEAK_BF16_TFLOPS * fig['clock_ghz'] / 2.4:.1f} TFLOP/s")
-        if "mfma_tflops_executed" in fig:
+            lines.append(f"  FLOP per launch ({what}, 2*d per visible pair each): {fl:.4e} -> {fl / ns / 1e3:.1f} "
+                         f"TFLOP/s at the trace average = {fl / ns / 1e3 / PEAK_BF16_TFLOPS:.4f} of peak")
+        has_mfma = fig["mfma_instructions"] > 0
+        if has_mfma:
+            lines.append(f"  MFMA busy per SIMD: {fig['mfma_busy']:.4f}; clock during the kernel {fig['clock_ghz']:.3f} "
+                         f"GHz (GRBM_GUI_ACTIVE per XCD / trace duration), bf16 peak at that clock "
+                         f"{PEAK_BF16_TFLOPS * fig['clock_ghz'] / 2.4:.1f} TFLOP/s")
+        else:
+            lines.append(f"  clock during the kernel {fig['clock_ghz']:.3f} GHz (GRBM_GUI_ACTIVE per XCD / trace duration)")
+        if "mfma_tflops_executed" in fig and has_mfma:
             lines.append(f"  MFMA FLOP executed per launch: {fig['mfma_flop_executed']:.4e} "
                          f"(SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512) -> {fig['mfma_tflops_executed']:.1f} TFLOP/s")
             lines.append(f"  transcendental lane-ops per launch: {fig['exp_lane_ops']:.4e} (SQ_INSTS_VALU_TRANS_F32 x 64) "
                          f"-> {fig['exp_lane_ops'] / ns:.4e} per ns = {fig['exp_lane_ops'] / ns / (256 * EXP_LANES_PER_CLK_CU * fig['clock_ghz']):.3f} "
                          f"of the transcendental rate at that clock ({EXP_LANES_PER_CLK_CU} lanes/clk/CU)")
             lines.append(f"  vector ALU busy per SIMD: {fig['valu_busy']:.3f} (4 x SQ_ACTIVE_INST_VALU quad-cycles / SIMD-cycles)")
-        lines.append(f"  VALU per MFMA {fig['valu_per_mfma']:.2f}; LDS instructions per MFMA {fig['lds_per_mfma']:.2f}; "
-                     f"LDS wait per wave-cycle {fig['lds_wait_per_wave_cycle']:.4f}")
+        if has_mfma:
+            lines.append(f"  VALU per MFMA {fig['valu_per_mfma']:.2f}; LDS instructions per MFMA {fig['lds_per_mfma']:.2f}; "
+                         f"LDS wait per wave-cycle {fig['lds_wait_per_wave_cycle']:.4f}")
         if "fetch_size_bytes" in fig and "write_size_bytes" in fig:
             tot = fig["fetch_size_bytes"] + fig["write_size_bytes"]
             lines.append(f"  calibration: torch's plain device copy of 1073741824 bytes gives bytes per counted byte "
