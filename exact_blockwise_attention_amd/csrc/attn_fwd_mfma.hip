@@ -17,8 +17,8 @@
 //     S accumulator to the P.V MFMA without leaving the registers;
 //   * V stays row-major in LDS; the V^T operand is gathered with the LDS transpose read ds_read_b64_tr_b16
 //     (within each 16-lane group, lane i receives column i of a 4-row x 16-column block);
-//   * O is normalised by the sum of the same bf16-rounded weights that enter P.V, formed on the matrix unit (one
-//     16x16x32 MFMA per 16 keys against a 0/1 selector); the log-sum-exp uses the sum of the fp32 weights;
+//   * one running sum of the fp32 weights gives both the normaliser of O and the log-sum-exp; the weights enter
+//     P.V rounded to bf16;
 //   * the reference maximum only moves when a row's new maximum exceeds it by more than 8 (log2 units), so most
 //     tiles skip the rescale of the accumulator; the weights stay below 2^8 and the result is unchanged (the
 //     final normalisation uses the same reference).
@@ -282,39 +282,21 @@ __device__ __forceinline__ void weights_tile(float (&w)[32], bf16x8 (&pb)[4], fl
   for (int kk = 0; kk < 4; ++kk) pb[kk] = pack_weights(w, kk);
 }
 
-// The row sum of the bf16-rounded weights (it normalises O) on the matrix unit. pb[kk] read as the B operand of
-// a 16x16x32 MFMA holds, in lane group g = l/16 and column n = l%16, keys 8*(g/2) .. +7 of query row n + 16*(g%2)
-// of the tile's 16-key group kk. Against the selector A[m][k] = 1 if (m/4)%2 == (k/8)%2, else 0, output row m,
-// column n is the group's weight sum of query row n + 16*((m/4)%2) -- and output register i of lane l is row
-// 4*(l/16) + i, column l%16: the sum of this lane's own query row l%32, in all four registers, over both key
-// halves. (The vector ALU's packed bf16 dot instructions would take the matrix pipeline from the P.V MFMAs.)
-__device__ __forceinline__ bf16x8 rowsum_selector(int lane) {
-  const __bf16 x = (((lane & 15) >> 2) & 1) == ((lane >> 4) & 1) ? (__bf16)1.0f : (__bf16)0.0f;
-  return bf16x8{x, x, x, x, x, x, x, x};
-}
-__device__ __forceinline__ f32x4 rowsum_mfma(const bf16x8& sel, const bf16x8& p, const f32x4& acc) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, p, acc, 0, 0, 0);
-}
-
-// Online softmax, second half: both running row sums. l_run sums the fp32 weights (it gives the log-sum-exp);
-// lq sums the bf16-rounded weights that enter P.V (it normalises O).
-__device__ __forceinline__ void sums_tile(const float (&w)[32], const bf16x8 (&pb)[4], const bf16x8& sel, float alpha,
-                                          float& l_run, f32x4& lq) {
+// Online softmax, second half: the running row sum of the fp32 weights (it normalises O and gives the
+// log-sum-exp).
+__device__ __forceinline__ void sums_tile(const float (&w)[32], float alpha, float& l_run) {
   float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int e = 0; e < 32; ++e) p[e & 3] += w[e];
   l_run = __builtin_fmaf(alpha, l_run, (p[0] + p[1]) + (p[2] + p[3]));
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) lq = rowsum_mfma(sel, pb[kk], lq);
 }
 
-// Rescales the accumulator and the bf16 weight sum when any lane's reference maximum moved.
+// Rescales the accumulator when any lane's reference maximum moved.
 template <int D>
-__device__ __forceinline__ void rescale_acc(f32x16 (&acc)[Geom<D>::CT], f32x4& lq, float alpha, bool need) {
+__device__ __forceinline__ void rescale_acc(f32x16 (&acc)[Geom<D>::CT], float alpha, bool need) {
   if (__builtin_amdgcn_ballot_w64(need)) {
 #pragma unroll
     for (int ct = 0; ct < Geom<D>::CT; ++ct) acc[ct] *= alpha;
-    lq *= alpha;
   }
 }
 
@@ -407,13 +389,12 @@ __device__ __forceinline__ void stage_phase1(const char* kn, const bf16x8 (&qf)[
 }
 
 // Phase 2: the 16 MFMAs of P.V for the current tile (its first V^T operands read in phase 1), beside the weights
-// of keys 32..63 (slots 0-7), their bf16 rounding (slots 5, 9; each needed three slots later) and both row sums
-// (the bf16 one on the matrix unit in slots 1, 5, 9, 13; the fp32 one in four partial sums, each started from
-// its first pair).
+// of keys 32..63 (slots 0-7), their bf16 rounding (slots 5, 9; each needed three slots later) and the row sum of
+// the fp32 weights (four partial sums, each started from its first pair).
 template <int D>
 __device__ __forceinline__ void stage_phase2(const char* vc, f32x16 (&acc)[Geom<D>::CT], const LaneAddr<D>& la,
                                              float (&w)[32], bf16x8 (&pb)[4], float alpha, float m_use,
-                                             float scale_log2, float& l_run, const bf16x8& sel, f32x4& lq,
+                                             float scale_log2, float& l_run,
                                              const bf16x8 (&vpre)[kLead]) {
   using G = Geom<D>;
   constexpr int NM = 4 * G::CT;
@@ -439,7 +420,6 @@ __device__ __forceinline__ void stage_phase2(const char* vc, f32x16 (&acc)[Geom<
     }
     if (j == 5) pb[2] = pack_weights(w, 2);
     if (j == 9) pb[3] = pack_weights(w, 3);
-    if ((j & 3) == 1) lq = rowsum_mfma(sel, pb[j >> 2], lq);
     pin(p[j & 3]);
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -462,7 +442,7 @@ __device__ __forceinline__ void load_q(const __bf16* Qblk, int rows_valid, int r
   }
 }
 
-// Epilogue: O = acc / lq, lse = ln2 * (m + log2 l); a row with no visible key gives (0, -inf). Register r of O^T
+// Epilogue: O = acc / l, lse = ln2 * (m + log2 l); a row with no visible key gives (0, -inf). Register r of O^T
 // tile ct holds head-dim column 32*ct + 8*(r/4) + 4*hi + r%4 of this lane's row; the buffer range of the
 // workgroup's block drops the stores of rows past Nq.
 // With MERGE the row is first merged with the running result (merge_o, merge_lse) by the log-sum-exp rule of
@@ -471,11 +451,11 @@ __device__ __forceinline__ void load_q(const __bf16* Qblk, int rows_valid, int r
 // output may alias the running result.
 template <int D, bool OF32, bool MERGE>
 __device__ __forceinline__ void store_out(const FwdArgs& a, int64_t bh, int q0, int block_rows, int local_row, int lane,
-                                          const f32x16 (&acc)[Geom<D>::CT], float m_ref, float l_run, float lq_tot) {
+                                          const f32x16 (&acc)[Geom<D>::CT], float m_ref, float l_run) {
   using G = Geom<D>;
   const int hi = lane >> 5;
   const float l_tot = pair_sum(l_run);
-  float inv = lq_tot > 0.0f ? 1.0f / lq_tot : 0.0f;
+  float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   const int qi = q0 + local_row;
   const int64_t o_rows = min(block_rows, a.Nq - q0);
   const int64_t base = (bh * (int64_t)a.Nq + q0) * D;
@@ -629,9 +609,9 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
     constexpr bool kPipe = pipelined<D>();
 
     if (ntiles > t0) {
-      issue_copy<D, true, kWaves>(K, t0 * kBN, a.Nk, k0, wave, lane);
-      issue_copy<D, false, kWaves>(V, t0 * kBN, a.Nk, v0, wave, lane);
-      if (kPipe && ntiles > t0 + 1) issue_copy<D, true, kWaves>(K, (t0 + 1) * kBN, a.Nk, k1, wave, lane);
+      issue_copy<D, true, kWaves>(K, t0 * kBN, kend, k0, wave, lane);
+      issue_copy<D, false, kWaves>(V, t0 * kBN, kend, v0, wave, lane);
+      if (kPipe && ntiles > t0 + 1) issue_copy<D, true, kWaves>(K, (t0 + 1) * kBN, kend, k1, wave, lane);
     }
     bf16x8 qf[G::KSTEPS];
     load_q<D>(reinterpret_cast<const __bf16*>(a.q) + (bh * (int64_t)a.Nq + q0) * D, min(kRows, a.Nq - q0),
@@ -644,8 +624,6 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
   #pragma unroll
     for (int ct = 0; ct < G::CT; ++ct) acc[ct] = f32x16{};
     float m_ref = -INFINITY, l_run = 0.0f;
-    f32x4 lq = {0.0f, 0.0f, 0.0f, 0.0f};
-    const bf16x8 rsel = rowsum_selector(lane);
 
     // One tile at a time (the last tile of a wave, tiles on the diagonal, and every tile when d < 128): scores,
     // mask, weights, rescale, P.V, sums.
@@ -657,10 +635,10 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
       if (partial) mask_scores(c0, c1, row_lim - t * kBN, row_lo - t * kBN);
       unpack_scores(c0, c1, w);
       weights_tile(w, pb, m_ref, alpha, need, a.scale_log2);
-      rescale_acc<D>(acc, lq, alpha, need);
+      rescale_acc<D>(acc, alpha, need);
       __builtin_amdgcn_sched_barrier(0);
       pv_tile<D, kPipe>(vc, pb, acc, la);
-      sums_tile(w, pb, rsel, alpha, l_run, lq);
+      sums_tile(w, alpha, l_run);
     };
 
     if constexpr (kPipe) {
@@ -678,8 +656,8 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
         __syncthreads();      // so have every wave's; every wave is done with K tile t and V tile t-1
         // K tile t+2 goes to the slot of K tile t, V tile t+1 to the slot of V tile t-1 (tiles past the end are
         // copied as zeros, which keeps the stage free of branches; nothing reads them)
-        const TileCopy<D, true, kWaves> ck(K, (t + 2) * kBN, a.Nk, kw, wave, lane);
-        const TileCopy<D, false, kWaves> cv(V, (t + 1) * kBN, a.Nk, vw, wave, lane);
+        const TileCopy<D, true, kWaves> ck(K, (t + 2) * kBN, kend, kw, wave, lane);
+        const TileCopy<D, false, kWaves> cv(V, (t + 1) * kBN, kend, vw, wave, lane);
         // A wave past its last visible tile writes zeros to n0/n1: every path then writes them, so the scores of
         // tile t, which reach this stage in c0/c1, are dead once unpacked and are not kept beside their copy.
         if (t >= nt_w) {
@@ -704,9 +682,9 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
         bf16x8 vpre[kLead];
         stage_phase1<D>(kn, qf, n0, n1, la, w, pb, m_ref, alpha, need, m_use, a.scale_log2, ck, cv, vc, vpre);
         __builtin_amdgcn_s_setprio(0);
-        rescale_acc<D>(acc, lq, alpha, need);
+        rescale_acc<D>(acc, alpha, need);
         __builtin_amdgcn_sched_barrier(0);
-        stage_phase2<D>(vc, acc, la, w, pb, alpha, m_use, a.scale_log2, l_run, rsel, lq, vpre);
+        stage_phase2<D>(vc, acc, la, w, pb, alpha, m_use, a.scale_log2, l_run, vpre);
       };
       for (int t = t0; t < ntiles; t += 2) {
         stage(t, sa0, sa1, sb0, sb1, k1, k0, v0, v1);
@@ -718,8 +696,8 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
         wait_vmem_all();      // this wave's copies of tile t have landed
         __syncthreads();      // every wave's copies have landed; every wave is done with tile t-1
         if (t + 1 < ntiles) {
-          issue_copy<D, true, kWaves>(K, (t + 1) * kBN, a.Nk, kn, wave, lane);
-          issue_copy<D, false, kWaves>(V, (t + 1) * kBN, a.Nk, vn, wave, lane);
+          issue_copy<D, true, kWaves>(K, (t + 1) * kBN, kend, kn, wave, lane);
+          issue_copy<D, false, kWaves>(V, (t + 1) * kBN, kend, vn, wave, lane);
         }
         if (t >= nt_w) return;
         f32x16 s0, s1;
@@ -731,7 +709,7 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
         if (t + 1 < ntiles) step(t + 1, k1, v1, k0, v0);
       }
     }
-    store_out<D, OF32, MERGE>(a, bh, q0, kRows, wave * 32 + (lane & 31), lane, acc, m_ref, l_run, lq[0]);
+    store_out<D, OF32, MERGE>(a, bh, q0, kRows, wave * 32 + (lane & 31), lane, acc, m_ref, l_run);
     if constexpr (!walks_blocks<D>()) break;
     // Every wave is done reading the LDS slots (its last reads fed the products just stored) before any wave copies
     // the next block's first tiles into them. A wave's copies land in issue order and each wave fills the same rows

@@ -33,8 +33,9 @@
  *             gives such a part zero weight.
  *   Dtypes    ATTN_BF16 inputs run on bf16 MFMA with fp32 accumulation and fp32 softmax statistics
  *             ("深度学习注意力机制优化与FlashAttention实践" §5.1 advises fp32 for the statistics); the softmax
- *             weights P are rounded to bf16 before the P.V product, and o is normalised by the sum of those
- *             rounded weights (a constant V comes back exactly), while lse uses the sum of the fp32 weights.
+ *             weights P are rounded to bf16 before the P.V product, and o and lse are both normalised by the sum
+ *             of the fp32 weights, so o carries the bf16 rounding of P: |o - exact| <= 2^-8 sum_j P_j |v_j|
+ *             before the output's own rounding (each weight rounded to nearest with 8 significant bits).
  *             ATTN_F32 inputs run in fp32 throughout.
  *   Asynchrony Every call only enqueues work on `stream`; nothing synchronises the device.
  *   Errors    Return ATTN_OK (0) or a negative code. Argument errors are detected before anything is
