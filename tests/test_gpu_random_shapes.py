@@ -6,8 +6,8 @@ head dim, causal or not, offsets, stride, window, output dtype), so that combina
 too: the forward, the backward, the fused merge (a running result over the first keys, a block over the rest)
 and the ring share (blocks of a global sequence in a drawn order, contiguous or striped, bf16 or fp32, with and
 without the exchange step). The draws are fixed by the seed; the bars are the same as in the other tests (bf16
-inputs: 2e-2 on o, 1e-3 on lse; fp32 inputs: 1e-5; gradients: 2e-2 max-abs and the per-element bound derived from
-the bf16 arithmetic, delta within the error propagated from the stored o).
+inputs: 2e-2 on o, 1e-3 on lse; fp32 inputs: 1e-5; gradients: the per-element bound derived from the bf16
+arithmetic, delta within the error propagated from the stored o).
 """
 import math
 
@@ -116,8 +116,11 @@ def test_random_backward(eb, i):
     q64, k64, v64, do64 = (bf16_bits_to_f64(x) for x in (q, k, v, do))
     omask = dict(causal=causal, q_off=q_off, k_off=k_off, stride=stride, window=window)
     ref = oracle.attention_backward(q64, k64, v64, do64, scale, **omask)
+    # The drawn shapes include few keys read by many query rows (e.g. 203 rows of two heads on 4 keys), where dk
+    # sums hundreds of terms and grows to |dk| ~ 12: one bf16 rounding of dS then moves it by more than a flat
+    # 2e-2, so the gradients here are held to the bound derived from the arithmetic, element by element.
     check_grads([host_f64(x) for x in (dq, dk, dv, delta)], ref, f"random backward {i} {case}", q64, k64, v64, do64,
-                host_f64(o), host_f64(lse), scale, omask, True, False)
+                host_f64(o), host_f64(lse), scale, omask, True, False, abs_bar=False)
 
 
 @pytest.mark.parametrize("i", range(len(MERGE_CASES)),
