@@ -14,9 +14,10 @@
 //     and walks the key tiles like the forward: S^T = K Q^T and dP^T = V dO^T put one query row in each lane
 //     (its lse and delta are per-lane scalars), dS^T is formed in registers and dQ^T += K^T dS^T. Before the
 //     loop it forms delta from O and dO and writes it out for the second kernel.
-//   * the dk/dv kernel owns 128 keys of one key/value head, 32 per wave with K and V held in VGPRs, and walks
-//     the query tiles of every query head that reads that key/value head: S = Q K^T and dP = dO V^T put one key
-//     in each lane, and dV^T += dO^T P, dK^T += Q^T dS.
+//   * the dk/dv kernel owns 128 keys of one key/value head, 32 per wave, and walks the query tiles of every
+//     query head that reads that key/value head: S = Q K^T and dP = dO V^T put one key in each lane, and
+//     dV^T += dO^T P, dK^T += Q^T dS. At d = 64 and 128 it runs eight waves with K and V in LDS, two waves per
+//     key range splitting each tile's rows; at d = 24 four waves with K and V in VGPRs.
 // Operand layout, shared by both kernels: the rows of the operand read from LDS by rows are taken in an order
 // with bits 2 and 3 of the row index swapped, which leaves the 32x32 MFMA results in registers already laid out
 // as the B operand of the next product (whose k index runs over those rows). The LDS tiles (64 rows of bf16)
@@ -64,10 +65,7 @@ struct BG {
   static constexpr int CPR = DP / 8;               // 16-byte chunks per LDS row
   static constexpr int CPG = D / 8;                // 16-byte chunks per row in memory (the rest read as zero)
   static constexpr int TILE = kBT * RB;
-  static constexpr int INSTR = TILE / 1024;        // wave-wide 16-byte-per-lane copies per tile
-  static constexpr int ROWS_PER_INSTR = 1024 / RB;
-  static constexpr int PER_WAVE = INSTR / kWaves;
-  static_assert(INSTR % kWaves == 0, "tile copy must split evenly over the waves");
+  static constexpr int ROWS_PER_INSTR = 1024 / RB; // rows per wave-wide 16-byte-per-lane copy
 };
 
 // Chunk swizzle of LDS row `row` (XOR on the 16-byte chunk index). Row reads: 16 consecutive lanes read one chunk
@@ -113,18 +111,22 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// This wave's share of the HBM -> LDS copy of rows [r0, r0 + 64) of X (rows_total rows of D bf16): natural row
-// order, chunks swizzled. Rows past rows_total read as zero (a tile wholly past the end touches no memory).
-template <int D>
+// This wave's share (of NW waves) of the HBM -> LDS copy of rows [r0, r0 + ROWS) of X (rows_total rows of D
+// bf16): natural row order, chunks swizzled. Rows past rows_total read as zero (a tile wholly past the end touches
+// no memory).
+template <int D, int ROWS = kBT, int NW = kWaves>
 __device__ __forceinline__ void copy_tile(const __bf16* X, int r0, int rows_total, char* dst, int wave, int lane) {
   using G = BG<D>;
-  const int valid = uniform_clamp(rows_total - r0, kBT);
+  constexpr int INSTR = ROWS * G::RB / 1024;       // wave-wide 16-byte-per-lane copies
+  static_assert(INSTR % NW == 0, "tile copy must split evenly over the waves");
+  constexpr int PER_WAVE = INSTR / NW;
+  const int valid = uniform_clamp(rows_total - r0, ROWS);
   // the range is in bytes of the rows in memory (D bf16 each), not of the padded LDS rows
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(X + (int64_t)r0 * D, (int64_t)valid * D * 2);
   const int sub = lane / G::CPR, pos = lane % G::CPR;
 #pragma unroll
-  for (int i = 0; i < G::PER_WAVE; ++i) {
-    const int instr = wave * G::PER_WAVE + i;
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int instr = wave * PER_WAVE + i;
     const int row = instr * G::ROWS_PER_INSTR + sub;
     const int m = pos ^ swz<D>(row);
     const uint32_t off = m < G::CPG ? (uint32_t)((row * D + m * 8) * 2) : kOutOfRange;
@@ -381,9 +383,10 @@ void attn_bwd_dq_kernel(BwdArgs a, int n_qtiles, int xcd_remap) {
 }
 
 // ------------------------------------------------------------------------------------------------------------
-// The dk/dv stages below are laid out slot by slot: one MFMA per slot, the LDS operand reads kLead slots ahead,
-// and a scheduling fence after every slot so that the compiler keeps the order (with few waves per SIMD nothing
-// else hides the LDS latency or the vector-ALU work). Register r of the score and dP accumulators s_h / p_h
+// The d = 24 dk/dv stage below is laid out slot by slot: one MFMA per slot, the LDS operand reads kLead slots
+// ahead, and a scheduling fence after every slot so that the compiler keeps the order (its stage is too short
+// for the other wave on the SIMD to hide the LDS latency and the vector-ALU work). Register r of the score and
+// dP accumulators s_h / p_h
 // (h = 0: tile rows 0..31, h = 1: rows 32..63) holds tile row 32*h + 16*(r/8) + 8*hi + r%8: operand group
 // kk = 2*h + r/8 and element r%8 of the lane's 8 rows 16*kk + 8*hi .. +7 (whose lse and delta are read from LDS
 // as two float4 each).
@@ -567,189 +570,13 @@ struct DkdvStage {
 };
 
 // ------------------------------------------------------------------------------------------------------------
-// The dk/dv stage for d = 64 and 128, pipelined across stages so that every phase of 2*KSTEPS MFMAs carries one
-// operand group's weights and score gradients (eight elements per lane) beside it. With PH = 2*KSTEPS slots per
-// phase, stage s runs
-//   phase 0: S, dP of rows 0..31 of stage s        beside group 3 (rows 48..63) of stage s - 1
-//   phase 1: dV, dK for groups 2, 3 of stage s - 1  beside group 0 (rows 0..15) of stage s
-//   phase 2: S, dP of rows 32..63 of stage s       beside group 1 (rows 16..31)
-//   phase 3: dV, dK for groups 0, 1 of stage s      beside group 2 (rows 32..47)
-// so a stage reads the Q and dO tiles of the stage before it too (three tile buffers), and the first stage and
-// a final drain half-stage leave out the parts that have no stage before or after them.
-template <int D>
-struct DkdvPipe {
-  using G = BG<D>;
-  static constexpr int PH = 2 * G::KSTEPS;        // slots per phase: the MFMAs of one S/dP half
-  static constexpr int NP = 2 * G::CT;            // MFMAs of one group's dV/dK
-  static_assert(PH == 2 * NP && PH >= 8, "the phase plan needs d = 64 or 128");
-  static constexpr int T = 4 * PH;
-  // a-step slot of element e of group g (g = 3: the previous stage's last group, in phase 0)
-  static constexpr int elem_slot(int g, int e) { return (g == 3 ? 0 : g + 1) * PH + 1 + (e * (PH - 3)) / 8; }
-  // lse and delta of group g: three slots before its first element (group 3's at the end of its own stage)
-  static constexpr int read_slot(int g) { return g == 3 ? T - 2 : elem_slot(g, 0) - 3; }
-
-  const bf16x8 (&kf)[G::KSTEPS];
-  const bf16x8 (&vf)[G::KSTEPS];
-  f32x16 (&dk)[G::CT];
-  f32x16 (&dv)[G::CT];
-  const Lanes<D>& la;
-  float scale_log2;
-
-  // carried from one stage to the next: the second S/dP half (its last group is formed in the next stage) and the
-  // bf16 operands of groups 2 and 3 (their dV/dK MFMAs run in the next stage)
-  f32x16 s0, s1, p0, p1;
-  bf16x8 pb[4], sb[4];
-  float x[8], dd[8], w[8], g[8];
-  bf16x2 wp[2][4], gp[2][4];
-  f32x4 lq[2][2], dl[2][2];
-  bf16x8 ring[kLead + 1];
-  // this stage's and the previous stage's tiles, this stage's rows and mask
-  const char *qc, *oc, *qp, *op;
-  const float *lc, *dc;
-  bool masked;
-  int lo, up;
-
-  template <bool PREV, bool CUR>
-  static constexpr bool has_mfma(int I) { return (I / PH == 1) ? PREV : CUR; }
-
-  template <bool PREV, bool CUR, int I>
-  __device__ __forceinline__ bf16x8 frag() const {
-    constexpr int ph = I / PH, j = I % PH;
-    if constexpr (ph == 0 || ph == 2) {
-      return row_frag<D>((j & 1) ? oc : qc, la, ph / 2, j >> 1);
-    } else if constexpr (ph == 1) {
-      constexpr int jj = j % NP;
-      return tr_frag<D>((jj & 1) ? qp : op, la, 2 + j / NP, jj >> 1);
-    } else {
-      constexpr int jj = j % NP;
-      return tr_frag<D>((jj & 1) ? qc : oc, la, j / NP, jj >> 1);
-    }
-  }
-
-  template <int GR, int E>
-  __device__ __forceinline__ void elem_a() {
-    constexpr int r = 8 * (GR & 1) + E;
-    const float sv = (GR >> 1) ? s1[r] : s0[r];
-    const float pv = (GR >> 1) ? p1[r] : p0[r];
-    x[E] = __builtin_fmaf(sv, scale_log2, -lq[GR & 1][E >> 2][E & 3]);
-    dd[E] = pv - dl[GR & 1][E >> 2][E & 3];
-    pin(x[E]);
-    pin(dd[E]);
-  }
-  template <int GR, int E>
-  __device__ __forceinline__ void elem_b() {
-    w[E] = __builtin_amdgcn_exp2f(x[E]);
-    pin(w[E]);
-  }
-  template <int GR, int E>
-  __device__ __forceinline__ void elem_c() {
-    g[E] = w[E] * dd[E];
-    if constexpr (E & 1) {
-      const f32x2 xw = {w[E - 1], w[E]}, yg = {g[E - 1], g[E]};
-      wp[GR & 1][E >> 1] = __builtin_convertvector(xw, bf16x2);
-      gp[GR & 1][E >> 1] = __builtin_convertvector(yg, bf16x2);
-      pin(wp[GR & 1][E >> 1]);
-      pin(gp[GR & 1][E >> 1]);
-    } else {
-      pin(g[E]);
-    }
-    if constexpr (E == 7) {
-      const bf16x2(&a)[4] = wp[GR & 1];
-      const bf16x2(&b)[4] = gp[GR & 1];
-      pb[GR] = __builtin_shufflevector(__builtin_shufflevector(a[0], a[1], 0, 1, 2, 3),
-                                       __builtin_shufflevector(a[2], a[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
-      sb[GR] = __builtin_shufflevector(__builtin_shufflevector(b[0], b[1], 0, 1, 2, 3),
-                                       __builtin_shufflevector(b[2], b[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
-    }
-  }
-  template <int I, int GR, int... Es>
-  __device__ __forceinline__ void group_steps(std::integer_sequence<int, Es...>) {
-    ((elem_slot(GR, Es) + 2 == I ? elem_c<GR, Es>() : void()), ...);
-    ((elem_slot(GR, Es) + 1 == I ? elem_b<GR, Es>() : void()), ...);
-    ((elem_slot(GR, Es) == I ? elem_a<GR, Es>() : void()), ...);
-  }
-  template <int GR>
-  __device__ __forceinline__ void read_rows() {
-    const int rb = 16 * GR + 8 * la.hi;
-    lq[GR & 1][0] = *reinterpret_cast<const f32x4*>(lc + rb);
-    lq[GR & 1][1] = *reinterpret_cast<const f32x4*>(lc + rb + 4);
-    dl[GR & 1][0] = *reinterpret_cast<const f32x4*>(dc + rb);
-    dl[GR & 1][1] = *reinterpret_cast<const f32x4*>(dc + rb + 4);
-  }
-  __device__ __forceinline__ void mask(f32x16& sm, int off) {
-    if (masked) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qr = off + 16 * (r >> 3) + (r & 7);
-        if (qr < lo || qr > up) sm[r] = -INFINITY;
-      }
-    }
-  }
-
-  template <bool PREV, bool CUR, int I>
-  __device__ __forceinline__ void slot() {
-    constexpr int ph = I / PH, j = I % PH;
-    if constexpr (I + kLead < T && has_mfma<PREV, CUR>(I + kLead)) ring[(I + kLead) % (kLead + 1)] = frag<PREV, CUR, I + kLead>();
-    if constexpr (has_mfma<PREV, CUR>(I)) {
-      const bf16x8 A = ring[I % (kLead + 1)];
-      if constexpr (ph == 0 || ph == 2) {
-        constexpr int ks = j >> 1;
-        f32x16& c = (j & 1) ? (ph == 0 ? p0 : p1) : (ph == 0 ? s0 : s1);
-        c = mfma(A, (j & 1) ? vf[ks] : kf[ks], ks == 0 ? f32x16{} : c);
-      } else {
-        constexpr int kk = (ph == 1 ? 2 : 0) + j / NP, jj = j % NP, ct = jj >> 1;
-        if constexpr (jj & 1) dk[ct] = mfma(A, sb[kk], dk[ct]);
-        else dv[ct] = mfma(A, pb[kk], dv[ct]);
-      }
-    }
-    if constexpr (CUR && I == read_slot(0)) read_rows<0>();
-    if constexpr (CUR && I == read_slot(1)) read_rows<1>();
-    if constexpr (CUR && I == read_slot(2)) read_rows<2>();
-    if constexpr (CUR && I == read_slot(3)) read_rows<3>();
-    if constexpr (CUR && I == PH - 1) {
-      __builtin_amdgcn_sched_barrier(0);
-      mask(s0, 0);
-    }
-    if constexpr (CUR && I == 3 * PH - 1) {
-      __builtin_amdgcn_sched_barrier(0);
-      mask(s1, 32);
-    }
-    if constexpr (PREV) group_steps<I, 3>(std::make_integer_sequence<int, 8>{});
-    if constexpr (CUR) {
-      group_steps<I, 0>(std::make_integer_sequence<int, 8>{});
-      group_steps<I, 1>(std::make_integer_sequence<int, 8>{});
-      group_steps<I, 2>(std::make_integer_sequence<int, 8>{});
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-
-  template <bool PREV, bool CUR, int... Is>
-  __device__ __forceinline__ void lead(std::integer_sequence<int, Is...>) {
-    ((has_mfma<PREV, CUR>(Is) ? (void)(ring[Is] = frag<PREV, CUR, Is>()) : void()), ...);
-  }
-  template <bool PREV, bool CUR, int... Is>
-  __device__ __forceinline__ void slots(std::integer_sequence<int, Is...>) {
-    (slot<PREV, CUR, Is>(), ...);
-  }
-  // One stage: PREV finishes the stage before (group 3 and its dV/dK for groups 2, 3), CUR runs this one. The
-  // drain (CUR false) stops after phase 1.
-  template <bool PREV, bool CUR>
-  __device__ __forceinline__ void stage() {
-    lead<PREV, CUR>(std::make_integer_sequence<int, kLead>{});
-    slots<PREV, CUR>(std::make_integer_sequence<int, CUR ? T : 2 * PH>{});
-  }
-};
-
-// ------------------------------------------------------------------------------------------------------------
-// dk/dv kernel: 128 keys of one key/value head per workgroup; query tiles of 64 of every query head in its group.
-
-// d = 64 and 128 hold K, V and both accumulators in registers at one wave per SIMD; d = 24 fits two.
-template <int D>
-constexpr int dkdv_waves() { return D >= 64 ? 1 : 2; }
-
+// dk/dv kernel at d = 24 (padded to 32): 128 keys of one key/value head per workgroup of four waves, 32 per wave
+// with K and V held in VGPRs (two waves per SIMD fit); query tiles of 64 of every query head in its group, one
+// DkdvStage per tile.
 template <int D, bool GF32>
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(dkdv_waves<D>(), dkdv_waves<D>())))
-void attn_bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int xcd_remap) {
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_dkdv24_kernel(BwdArgs a, int n_ktiles, int xcd_remap) {
+  static_assert(D == 24, "d = 64 and 128 take attn_bwd_dkdv_kernel");
   using G = BG<D>;
   __shared__ __attribute__((aligned(1024))) char qa[G::TILE];
   __shared__ __attribute__((aligned(1024))) char qb[G::TILE];
@@ -763,8 +590,6 @@ void attn_bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int xcd_remap) {
   __shared__ __attribute__((aligned(16))) float rlb[kBT];
   __shared__ __attribute__((aligned(16))) float rda[kBT];
   __shared__ __attribute__((aligned(16))) float rdb[kBT];
-  __shared__ __attribute__((aligned(1024))) char qc_[D >= 64 ? G::TILE : 16];   // third tile buffers (d >= 64)
-  __shared__ __attribute__((aligned(1024))) char oc_[D >= 64 ? G::TILE : 16];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -849,75 +674,242 @@ void attn_bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int xcd_remap) {
     dv[ct] = f32x16{};
   }
 
-  if constexpr (D >= 64) {
-    // Stage s keeps its tiles in buffer s % 3 (it also reads stage s - 1's) and its rows in slot s % 2. After the
-    // barrier that opens stage s every wave is done with stage s - 1, so the copies of stage s + 1 may overwrite
-    // buffer (s + 1) % 3 = (s - 2) % 3. Every wave runs every stage, also one whose rows none of its keys see (the
-    // mask then hides them all): the stage after it finishes that stage's last group.
-    DkdvPipe<D> P{kf, vf, dk, dv, la, a.scale_log2};
-    auto qt = [&](int b) { return b == 0 ? qa : b == 1 ? qb : qc_; };
-    auto ot = [&](int b) { return b == 0 ? oa : b == 1 ? ob : oc_; };
-    auto run = [&](auto prev, int s, int b) {
-      wait_vmem_all();
-      __syncthreads();
-      const int bn = b == 2 ? 0 : b + 1, bp = b == 0 ? 2 : b - 1;
-      const bool more = s + 1 < nstages;
-      if (more) issue_stage(s + 1, qt(bn), ot(bn));
-      if (wave == 0 && s + 2 < nstages) issue_rows(s + 2, (s & 1) ? rlb : rla, (s & 1) ? rdb : rda);
-      const int i0 = (t0 + s % nt) * kBT;
-      P.qc = qt(b);
-      P.oc = ot(b);
-      P.qp = qt(bp);
-      P.op = ot(bp);
-      P.lc = (s & 1) ? lb_ : la_;
-      P.dc = (s & 1) ? db_ : da_;
-      P.masked = !(i0 >= all_lo && i0 + kBT - 1 <= all_hi);
-      P.lo = vis_lo - i0;
-      P.up = vis_hi - i0;
-      P.template stage<decltype(prev)::value, true>();
-      if (more && wave == 0)
-        convert_rows(s + 1, (s & 1) ? rla : rlb, (s & 1) ? rda : rdb, (s & 1) ? la_ : lb_, (s & 1) ? da_ : db_);
-    };
-    if (nstages > 0) {
-      run(std::false_type{}, 0, 0);
-      for (int s = 1; s < nstages; s += 3) {
-        run(std::true_type{}, s, 1);
-        if (s + 1 < nstages) run(std::true_type{}, s + 1, 2);
-        if (s + 2 < nstages) run(std::true_type{}, s + 2, 0);
-      }
-      // the last stage's final group and its dV/dK (its tiles stay in place: nothing more is copied)
-      const int bl = (nstages - 1) % 3;
-      P.qp = qt(bl);
-      P.op = ot(bl);
-      P.template stage<true, false>();
-    }
-  } else {
-    // stage s: tiles in (qc, oc), converted rows in (lc, dc); the next stage's tiles go to (qn, on) and its rows
-    // are converted from the raw slot (rn_l, rn_d) into (ln, dn); the raw rows of stage s + 2 go to (rs_l, rs_d),
-    // the raw slot stage s used
-    auto step = [&](int s, const char* qc, const char* oc, const float* lc, const float* dc, char* qn, char* on,
-                    float* ln, float* dn, const float* rn_l, const float* rn_d, float* rs_l, float* rs_d) {
-      wait_vmem_all();      // this wave's copies of stage s (tiles) and s + 1 (raw rows) have landed
-      __syncthreads();      // every wave's have; every wave is done with stage s - 1
-      const bool more = s + 1 < nstages;
-      if (more) issue_stage(s + 1, qn, on);
-      if (wave == 0 && s + 2 < nstages) issue_rows(s + 2, rs_l, rs_d);
-      const int i0 = (t0 + s % nt) * kBT;
-      if (i0 + kBT - 1 >= any_lo && i0 <= any_hi)
-        DkdvStage<D>{qc, oc, lc, dc, kf, vf, dk, dv, la, a.scale_log2, !(i0 >= all_lo && i0 + kBT - 1 <= all_hi),
-                     vis_lo - i0, vis_hi - i0}();
-      if (more && wave == 0) convert_rows(s + 1, rn_l, rn_d, ln, dn);
-    };
-    for (int s = 0; s < nstages; s += 2) {
-      step(s, qa, oa, la_, da_, qb, ob, lb_, db_, rlb, rdb, rla, rda);
-      if (s + 1 < nstages) step(s + 1, qb, ob, lb_, db_, qa, oa, la_, da_, rla, rda, rlb, rdb);
-    }
+  // stage s: tiles in (qc, oc), converted rows in (lc, dc); the next stage's tiles go to (qn, on) and its rows
+  // are converted from the raw slot (rn_l, rn_d) into (ln, dn); the raw rows of stage s + 2 go to (rs_l, rs_d),
+  // the raw slot stage s used
+  auto step = [&](int s, const char* qc, const char* oc, const float* lc, const float* dc, char* qn, char* on,
+                  float* ln, float* dn, const float* rn_l, const float* rn_d, float* rs_l, float* rs_d) {
+    wait_vmem_all();      // this wave's copies of stage s (tiles) and s + 1 (raw rows) have landed
+    __syncthreads();      // every wave's have; every wave is done with stage s - 1
+    const bool more = s + 1 < nstages;
+    if (more) issue_stage(s + 1, qn, on);
+    if (wave == 0 && s + 2 < nstages) issue_rows(s + 2, rs_l, rs_d);
+    const int i0 = (t0 + s % nt) * kBT;
+    if (i0 + kBT - 1 >= any_lo && i0 <= any_hi)
+      DkdvStage<D>{qc, oc, lc, dc, kf, vf, dk, dv, la, a.scale_log2, !(i0 >= all_lo && i0 + kBT - 1 <= all_hi),
+                   vis_lo - i0, vis_hi - i0}();
+    if (more && wave == 0) convert_rows(s + 1, rn_l, rn_d, ln, dn);
+  };
+  for (int s = 0; s < nstages; s += 2) {
+    step(s, qa, oa, la_, da_, qb, ob, lb_, db_, rlb, rdb, rla, rda);
+    if (s + 1 < nstages) step(s + 1, qb, ob, lb_, db_, qa, oa, la_, da_, rla, rda, rlb, rdb);
   }
   const int64_t kvrow = kvbh * (int64_t)a.Nk;
   store_grad<D, GF32>(reinterpret_cast<char*>(a.dk) + kvrow * D * (GF32 ? 4 : 2), kw0, a.Nk, lane, dk, a.scale,
                       a.accumulate != 0);
   store_grad<D, GF32>(reinterpret_cast<char*>(a.dv) + kvrow * D * (GF32 ? 4 : 2), kw0, a.Nk, lane, dv, 1.0f,
                       a.accumulate != 0);
+}
+
+// ------------------------------------------------------------------------------------------------------------
+// dk/dv kernel at d = 64 and 128, two waves per SIMD: 128 keys of one key/value head per workgroup of eight
+// waves. K and V of the block sit in LDS for the whole kernel (their B-operand fragments are read from there at
+// each use, which frees the 64 registers they would take); waves w and w + 4 own the same 32 keys and split each
+// 64-row query tile, w taking rows 0..31 and w + 4 rows 32..63, each with its own dK and dV accumulators, which
+// the pair adds up through LDS at the end. A wave's stage is 4*KSTEPS MFMAs: S and dP (2*KSTEPS, contraction over
+// the head dim), then dV^T += dO^T P and dK^T += Q^T dS over its 32 rows (2*KSTEPS); the compiler schedules it,
+// and the other wave on the SIMD fills the gaps of the element work between them. Register r of the score and dP
+// accumulators holds row 16*(r/8) + 8*hi + r%8 of the wave's 32 (the row operand is read in perm_row order).
+constexpr int kW2 = 8;   // waves per workgroup
+
+template <int D, bool GF32>
+__global__ __launch_bounds__(64 * kW2) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int xcd_remap) {
+  static_assert(D == 64 || D == 128, "d = 24 takes attn_bwd_dkdv24_kernel");
+  using G = BG<D>;
+  constexpr int KV = kOwn * G::RB;                // 128 key rows of K (or V)
+  // Every LDS buffer is an array of its own: the compiler then knows which one a copy in flight writes, and does
+  // not make the reads of the current stage's tiles wait for the copies of the next stage.
+  __shared__ __attribute__((aligned(1024))) char kb[KV];
+  __shared__ __attribute__((aligned(1024))) char vb[KV];
+  __shared__ __attribute__((aligned(1024))) char qa[G::TILE];
+  __shared__ __attribute__((aligned(1024))) char qb[G::TILE];
+  __shared__ __attribute__((aligned(1024))) char oa[G::TILE];
+  __shared__ __attribute__((aligned(1024))) char ob[G::TILE];
+  __shared__ __attribute__((aligned(16))) float la_[kBT];   // exp2-domain lse of the tile rows, slot a
+  __shared__ __attribute__((aligned(16))) float lb_[kBT];
+  __shared__ __attribute__((aligned(16))) float da_[kBT];   // delta of the tile rows
+  __shared__ __attribute__((aligned(16))) float db_[kBT];
+  __shared__ __attribute__((aligned(16))) float rla[kBT];   // raw lse and delta as copied, slots a and b
+  __shared__ __attribute__((aligned(16))) float rlb[kBT];
+  __shared__ __attribute__((aligned(16))) float rda[kBT];
+  __shared__ __attribute__((aligned(16))) float rdb[kBT];
+  // the pair exchange at the end reuses K, V and the tiles: one fp32 gradient of 32 keys per slot
+  constexpr int XCH = 32 * D * 4;
+  static_assert(2 * XCH == KV && XCH == G::TILE, "exchange slots: two in K, two in V, one per tile");
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kw = wave & 3, half = wave >> 2;     // owned keys 32*kw.., tile rows 32*half..
+  int64_t kvbh;
+  int kt;
+  decode_block(n_ktiles, xcd_remap, kvbh, kt);   // ascending key tiles: under a causal mask the first see most
+  const int k0 = kt * kOwn;
+  const int kw0 = k0 + kw * 32;
+  const int group = a.kv_group;
+  const int64_t bh0 = kvbh * group;
+
+  int qbeg = 0, qend = a.Nq;
+  if (a.causal) {
+    qbeg = max(0, k0 - a.diag);
+    if (a.lo != kNoWindow) qend = min(a.Nq, k0 + kOwn - 1 - a.lo + 1);
+  }
+  const int t0 = qbeg / kBT;
+  const int nt = qend > qbeg ? (qend + kBT - 1) / kBT - t0 : 0;
+  const int nstages = nt * group;
+
+  const __bf16* Q = reinterpret_cast<const __bf16*>(a.q);
+  const __bf16* dO = reinterpret_cast<const __bf16*>(a.dout);
+  auto issue_stage = [&](int s, char* qd, char* od) {
+    const int64_t bh = bh0 + s / nt;
+    const int r0 = (t0 + s % nt) * kBT;
+    copy_tile<D, kBT, kW2>(Q + bh * a.Nq * D, r0, a.Nq, qd, wave, lane);
+    copy_tile<D, kBT, kW2>(dO + bh * a.Nq * D, r0, a.Nq, od, wave, lane);
+  };
+  // lse and delta of a stage's rows: copied raw two stages ahead and converted one stage ahead, by wave 0
+  auto issue_rows = [&](int s, float* rl, float* rd) {
+    const int64_t bh = bh0 + s / nt;
+    const int r0 = (t0 + s % nt) * kBT;
+    const int valid = uniform_clamp(a.Nq - r0, kBT);
+    const __amdgpu_buffer_rsrc_t r1 = make_rsrc(a.lse + bh * a.Nq + r0, (int64_t)valid * 4);
+    const __amdgpu_buffer_rsrc_t r2 = make_rsrc(a.delta + bh * a.Nq + r0, (int64_t)valid * 4);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r1, (lds_void*)rl, 4, (uint32_t)(lane * 4), 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r2, (lds_void*)rd, 4, (uint32_t)(lane * 4), 0, 0, 0);
+  };
+  auto convert_rows = [&](int s, const float* rl, const float* rd, float* lq, float* dq) {
+    const int i = (t0 + s % nt) * kBT + lane;
+    lq[lane] = i < a.Nq ? lse_to_sub(rl[lane]) : INFINITY;
+    dq[lane] = i < a.Nq ? rd[lane] : 0.0f;
+  };
+
+  const __bf16* Ks = reinterpret_cast<const __bf16*>(a.k) + kvbh * (int64_t)a.Nk * D;
+  const __bf16* Vs = reinterpret_cast<const __bf16*>(a.v) + kvbh * (int64_t)a.Nk * D;
+  if (nstages > 0) {
+    copy_tile<D, kOwn, kW2>(Ks, k0, a.Nk, kb, wave, lane);
+    copy_tile<D, kOwn, kW2>(Vs, k0, a.Nk, vb, wave, lane);
+    issue_stage(0, qa, oa);
+    if (wave == 0) {
+      issue_rows(0, rla, rda);
+      if (nstages > 1) issue_rows(1, rlb, rdb);
+      wait_vmem_all();
+      convert_rows(0, rla, rda, la_, da_);
+    }
+  }
+
+  const Lanes<D> la(lane);
+  const int hi = lane >> 5;
+  // B operand of this wave's keys (K or V in LDS): key 32*kw + l%32 (natural order), head-dim columns
+  // 16*ks + 8*hi .. +7
+  const int krow = 32 * kw + (lane & 31);
+  const int koff = krow * G::RB, ksw = swz<D>(krow);
+  auto key_frag = [&](const char* t, int ks) {
+    return *reinterpret_cast<const bf16x8*>(t + koff + 16 * ((2 * ks + hi) ^ ksw));
+  };
+  const int key = kw0 + (lane & 31);
+  const int vis_lo = (a.causal ? key - a.diag : -(1 << 30)) - 8 * hi;
+  const int vis_hi = (a.causal && a.lo != kNoWindow ? key - a.lo : (1 << 30)) - 8 * hi;
+  const int all_lo = a.causal ? kw0 + 31 - a.diag : -(1 << 30);
+  const int all_hi = a.causal && a.lo != kNoWindow ? kw0 - a.lo : (1 << 30);
+  const int any_lo = a.causal ? kw0 - a.diag : -(1 << 30);
+  const int any_hi = a.causal && a.lo != kNoWindow ? kw0 + 31 - a.lo : (1 << 30);
+
+  f32x16 dk[G::CT], dv[G::CT];
+#pragma unroll
+  for (int ct = 0; ct < G::CT; ++ct) {
+    dk[ct] = f32x16{};
+    dv[ct] = f32x16{};
+  }
+
+  // stage s: tiles in (qc, oc), converted rows in (lc, dc); as in the one-stage kernel above
+  auto step = [&](int s, const char* qc, const char* oc, const float* lc, const float* dc, char* qn, char* on,
+                  float* ln, float* dn, const float* rn_l, const float* rn_d, float* rs_l, float* rs_d) {
+    wait_vmem_all();      // this wave's copies of stage s (tiles) and s + 1 (raw rows) have landed
+    __syncthreads();      // every wave's have; every wave is done with stage s - 1
+    const bool more = s + 1 < nstages;
+    if (more) issue_stage(s + 1, qn, on);
+    if (wave == 0 && s + 2 < nstages) issue_rows(s + 2, rs_l, rs_d);
+    const int r0 = (t0 + s % nt) * kBT + 32 * half;   // this wave's first row
+    if (r0 + 31 >= any_lo && r0 <= any_hi && r0 < a.Nq) {
+      f32x16 sc = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < G::KSTEPS; ++ks) {
+        sc = mfma(row_frag<D>(qc, la, half, ks), key_frag(kb, ks), sc);
+        dp = mfma(row_frag<D>(oc, la, half, ks), key_frag(vb, ks), dp);
+      }
+      // register r holds row r0 + 16*(r/8) + 8*hi + r%8 of this lane's key
+      if (!(r0 >= all_lo && r0 + 31 <= all_hi)) {
+        const int lo = vis_lo - r0, up = vis_hi - r0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qr = 16 * (r >> 3) + (r & 7);
+          if (qr < lo || qr > up) sc[r] = -INFINITY;
+        }
+      }
+      bf16x8 pb[2], sb[2];
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int rb = 32 * half + 16 * g + 8 * hi;
+        const f32x4 l0 = *reinterpret_cast<const f32x4*>(lc + rb), l1 = *reinterpret_cast<const f32x4*>(lc + rb + 4);
+        const f32x4 d0 = *reinterpret_cast<const f32x4*>(dc + rb), d1 = *reinterpret_cast<const f32x4*>(dc + rb + 4);
+        f32x8 w, gr;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float lq = e < 4 ? l0[e] : l1[e - 4];
+          const float dl = e < 4 ? d0[e] : d1[e - 4];
+          w[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * g + e], a.scale_log2, -lq));
+          gr[e] = w[e] * (dp[8 * g + e] - dl);
+        }
+        pb[g] = __builtin_convertvector(w, bf16x8);
+        sb[g] = __builtin_convertvector(gr, bf16x8);
+      }
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int ct = 0; ct < G::CT; ++ct) {
+          dv[ct] = mfma(tr_frag<D>(oc, la, 2 * half + g, ct), pb[g], dv[ct]);
+          dk[ct] = mfma(tr_frag<D>(qc, la, 2 * half + g, ct), sb[g], dk[ct]);
+        }
+    }
+    if (more && wave == 0) convert_rows(s + 1, rn_l, rn_d, ln, dn);
+  };
+  for (int s = 0; s < nstages; s += 2) {
+    step(s, qa, oa, la_, da_, qb, ob, lb_, db_, rlb, rdb, rla, rda);
+    if (s + 1 < nstages) step(s + 1, qb, ob, lb_, db_, qa, oa, la_, da_, rla, rda, rlb, rdb);
+  }
+
+  // Pair exchange: wave w + 4 hands its dV to wave w, wave w hands its dK to wave w + 4; each adds its partner's
+  // part and stores one gradient. Register r of tile ct sits at float4 index (4*ct + r/4)*64 + lane of the slot.
+  wait_vmem_all();        // no copy into LDS is still in flight (none is after a stage; this is for clarity)
+  __syncthreads();        // every wave is done with the tiles (and K, V) the exchange overwrites
+  float* xv = reinterpret_cast<float*>(kw < 2 ? kb + kw * XCH : vb + (kw - 2) * XCH);   // dV of pair kw
+  float* xk = reinterpret_cast<float*>(kw == 0 ? qa : kw == 1 ? qb : kw == 2 ? oa : ob);  // dK of pair kw
+  f32x16 (&mine)[G::CT] = half ? dv : dk;
+  float* out_x = half ? xv : xk;
+#pragma unroll
+  for (int ct = 0; ct < G::CT; ++ct)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 y = {mine[ct][4 * g], mine[ct][4 * g + 1], mine[ct][4 * g + 2], mine[ct][4 * g + 3]};
+      *reinterpret_cast<f32x4*>(out_x + ((4 * ct + g) * 64 + lane) * 4) = y;
+    }
+  __syncthreads();
+  f32x16 (&keep)[G::CT] = half ? dk : dv;
+  const float* in_x = half ? xk : xv;
+#pragma unroll
+  for (int ct = 0; ct < G::CT; ++ct)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 y = *reinterpret_cast<const f32x4*>(in_x + ((4 * ct + g) * 64 + lane) * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) keep[ct][4 * g + e] += y[e];
+    }
+  const int64_t kvrow = kvbh * (int64_t)a.Nk;
+  if (half)
+    store_grad<D, GF32>(reinterpret_cast<char*>(a.dk) + kvrow * D * (GF32 ? 4 : 2), kw0, a.Nk, lane, dk, a.scale,
+                        a.accumulate != 0);
+  else
+    store_grad<D, GF32>(reinterpret_cast<char*>(a.dv) + kvrow * D * (GF32 ? 4 : 2), kw0, a.Nk, lane, dv, 1.0f,
+                        a.accumulate != 0);
 }
 
 template <int D, bool GF32>
@@ -936,8 +928,12 @@ hipError_t launch_d(const BwdArgs& a, hipStream_t stream) {
     const int n_ktiles = (a.Nk + kOwn - 1) / kOwn;
     const int64_t total = (int64_t)n_ktiles * BHkv;
     if (total > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, GF32>), dim3((unsigned)total), dim3(64 * kWaves), 0, stream, a,
-                       n_ktiles, total % 8 == 0 ? 1 : 0);
+    if constexpr (D >= 64)
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, GF32>), dim3((unsigned)total), dim3(64 * kW2), 0, stream, a,
+                         n_ktiles, total % 8 == 0 ? 1 : 0);
+    else
+      hipLaunchKernelGGL((attn_bwd_dkdv24_kernel<D, GF32>), dim3((unsigned)total), dim3(64 * kWaves), 0, stream, a,
+                         n_ktiles, total % 8 == 0 ? 1 : 0);
     return hipGetLastError();
   }
   return hipSuccess;
