@@ -337,7 +337,8 @@ template <int D, class CopyK, class CopyV>
 __device__ __forceinline__ void stage_phase1(const char* kn, const bf16x8 (&qf)[Geom<D>::KSTEPS], f32x16& n0,
                                              f32x16& n1, const LaneAddr<D>& la, float (&w)[32], bf16x8 (&pb)[4],
                                              float& m_ref, float& alpha, bool& need, float& m_use, float scale_log2,
-                                             const CopyK& ck, const CopyV& cv, const char* vc, bf16x8 (&vpre)[kLead]) {
+                                             const CopyK& ck, const CopyV& cv, const char* vc, bf16x8 (&vpre)[kLead],
+                                             bool skipmax) {
   constexpr int NM = 2 * Geom<D>::KSTEPS;
   static_assert(NM == 16, "the slot plan below is laid out for 16 MFMAs per phase");
   static_assert(CopyK::kPerWave <= 4 && CopyV::kPerWave <= 4, "one tile-copy instruction per even slot");
@@ -362,14 +363,23 @@ __device__ __forceinline__ void stage_phase1(const char* kn, const bf16x8 (&qf)[
     if (i < 4) {
       // IEEE maximum (v_maximum3_f32): no NaN quieting of the MFMA results is needed before it. One chain over
       // the 32 scores, two more per instruction (16 instructions; a tree of pairs takes 23).
-      float m = i == 0 ? __builtin_elementwise_maximum(w[0], w[1])
-                       : __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, w[8 * i]), w[8 * i + 1]);
+      if (!skipmax) {
+        float m = i == 0 ? __builtin_elementwise_maximum(w[0], w[1])
+                         : __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, w[8 * i]), w[8 * i + 1]);
 #pragma unroll
-      for (int e = 2; e < 8; e += 2)
-        m = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m, w[8 * i + e]), w[8 * i + e + 1]);
-      mx = m;
+        for (int e = 2; e < 8; e += 2)
+          m = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m, w[8 * i + e]), w[8 * i + e + 1]);
+        mx = m;
+      }
     } else if (i == 4) {
-      update_reference(mx, m_ref, alpha, need, m_use, scale_log2);
+      if (!skipmax) {
+        update_reference(mx, m_ref, alpha, need, m_use, scale_log2);
+      } else {
+        // the reference stays where it is (finite in every lane: the caller checks)
+        alpha = 1.0f;
+        need = false;
+        m_use = m_ref;
+      }
     } else if (i < 13) {
       const int e = 2 * (i - 5);
       w[e] = weight(w[e], scale_log2, m_use);
@@ -608,11 +618,14 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
     const int nlow = low_edge > 0 ? (low_edge + kBN - 1) / kBN : 0;
     constexpr bool kPipe = pipelined<D>();
 
-    if (ntiles > t0) {
-      issue_copy<D, true, kWaves>(K, t0 * kBN, kend, k0, wave, lane);
-      issue_copy<D, false, kWaves>(V, t0 * kBN, kend, v0, wave, lane);
-      if (kPipe && ntiles > t0 + 1) issue_copy<D, true, kWaves>(K, (t0 + 1) * kBN, kend, k1, wave, lane);
-    }
+    auto first_copies = [&]() {
+      if (ntiles > t0) {
+        issue_copy<D, true, kWaves>(K, t0 * kBN, kend, k0, wave, lane);
+        issue_copy<D, false, kWaves>(V, t0 * kBN, kend, v0, wave, lane);
+        if (kPipe && ntiles > t0 + 1) issue_copy<D, true, kWaves>(K, (t0 + 1) * kBN, kend, k1, wave, lane);
+      }
+    };
+    first_copies();
     bf16x8 qf[G::KSTEPS];
     load_q<D>(reinterpret_cast<const __bf16*>(a.q) + (bh * (int64_t)a.Nq + q0) * D, min(kRows, a.Nq - q0),
               wave * 32, lane, qf);
@@ -646,10 +659,15 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
       // weights, then P.V of tile t (V tile t) beside the rest of tile t's softmax. K tiles therefore arrive one
       // tile ahead of V tiles: after the barrier of stage t, K tile t+2 is copied into the slot of K tile t and V
       // tile t+1 into the slot of V tile t-1.
+      //
+      // Speculative reference: from the third tile of a block on, the row maximum is not formed and every lane's
+      // weights are taken against the reference the first two tiles set (its rows' largest visible scores so
+      // far). Weights then come out as large as 2^(row maximum - reference) instead of at most 2^slack; in fp32
+      // and bf16 that changes no relative rounding, only the common scale of acc and l, which the epilogue divides
+      // out. Only an overflow would do harm, so the block is redone with the row maximum formed at every tile
+      // (the exact lazy rescaling above) when any wave's l or acc ends non-finite.
       f32x16 sa0, sa1, sb0, sb1;
-      wait_vmem_all();
-      __syncthreads();
-      if (nt_w > t0) qk_tile<D, true>(k0, qf, sa0, sa1, la);
+      bool spec = true;
       auto stage = [&](int t, f32x16& c0, f32x16& c1, f32x16& n0, f32x16& n1, const char* kn, char* kw,
                        const char* vc, char* vw) {
         wait_vmem_all();      // this wave's copies of K tile t+1 and V tile t have landed
@@ -680,15 +698,38 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
         // so the issue arbiter favours it over the SIMD's other wave (measured: +2.5 % causal, +0.7 % unmasked).
         __builtin_amdgcn_s_setprio(1);
         bf16x8 vpre[kLead];
-        stage_phase1<D>(kn, qf, n0, n1, la, w, pb, m_ref, alpha, need, m_use, a.scale_log2, ck, cv, vc, vpre);
+        // wave-uniform; a lane whose rows have seen no visible key yet keeps the reference update
+        const bool skipmax = spec && t >= t0 + 2 && !__builtin_amdgcn_ballot_w64(m_ref == -INFINITY);
+        stage_phase1<D>(kn, qf, n0, n1, la, w, pb, m_ref, alpha, need, m_use, a.scale_log2, ck, cv, vc, vpre,
+                        skipmax);
         __builtin_amdgcn_s_setprio(0);
         rescale_acc<D>(acc, alpha, need);
         __builtin_amdgcn_sched_barrier(0);
         stage_phase2<D>(vc, acc, la, w, pb, alpha, m_use, a.scale_log2, l_run, vpre);
       };
-      for (int t = t0; t < ntiles; t += 2) {
-        stage(t, sa0, sa1, sb0, sb1, k1, k0, v0, v1);
-        if (t + 1 < ntiles) stage(t + 1, sb0, sb1, sa0, sa1, k0, k1, v1, v0);
+      for (;;) {
+        wait_vmem_all();
+        __syncthreads();
+        if (nt_w > t0) qk_tile<D, true>(k0, qf, sa0, sa1, la);
+        for (int t = t0; t < ntiles; t += 2) {
+          stage(t, sa0, sa1, sb0, sb1, k1, k0, v0, v1);
+          if (t + 1 < ntiles) stage(t + 1, sb0, sb1, sa0, sa1, k0, k1, v1, v0);
+        }
+        if (!spec) break;
+        float chk = l_run;
+#pragma unroll
+        for (int ct = 0; ct < G::CT; ++ct)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) chk += acc[ct][r];
+        // every wave's copies (the last stages copy zero tiles past the end) land before any wave starts over
+        wait_vmem_all();
+        if (!__syncthreads_or(!__builtin_isfinite(chk))) break;
+        spec = false;
+#pragma unroll
+        for (int ct = 0; ct < G::CT; ++ct) acc[ct] = f32x16{};
+        m_ref = -INFINITY;
+        l_run = 0.0f;
+        first_copies();
       }
     } else {
       // One tile per step: after the barrier of tile t, tile t+1 is copied into the slots tile t-1 left.
