@@ -328,11 +328,11 @@ __device__ __forceinline__ void pv_tile(const char* vt, const bf16x8 (&pb)[4], f
 // lists its instructions slot by slot -- one MFMA, the LDS reads two MFMAs ahead, and a slice of the softmax work
 // of the current tile -- with a scheduling fence after every slot so that the compiler keeps that order.
 //
-// Phase 1: the 16 MFMAs of the next tile's scores, beside the current tile's row maximum (slots 0-3), reference
-// update (slot 4), the weights of keys 0..31 (slots 5-12) and their bf16 rounding (slots 10, 14); the even slots
-// also issue this wave's share of the copies of K tile t+2 and V tile t+1, and the last three slots, whose vector
-// work is light, read phase 2's first V^T operands (the V tile is resident since the stage's barrier), so that
-// phase 2 does not open with a wait on the LDS.
+// Phase 1: the 16 MFMAs of the next tile's scores, beside the current tile's row maximum (slots 0-3) and reference
+// update (slot 4) unless `skipmax` keeps the reference as it is, the weights of keys 0..31 (slots 5-12) and their
+// bf16 rounding (slots 10, 14); the even slots also issue this wave's share of the copies of K tile t+2 and V
+// tile t+1, and the last three slots, whose vector work is light, read phase 2's first V^T operands (the V tile
+// is resident since the stage's barrier), so that phase 2 does not open with a wait on the LDS.
 template <int D, class CopyK, class CopyV>
 __device__ __forceinline__ void stage_phase1(const char* kn, const bf16x8 (&qf)[Geom<D>::KSTEPS], f32x16& n0,
                                              f32x16& n1, const LaneAddr<D>& la, float (&w)[32], bf16x8 (&pb)[4],
