@@ -36,6 +36,10 @@
  *             weights P are rounded to bf16 before the P.V product, and o and lse are both normalised by the sum
  *             of the fp32 weights, so o carries the bf16 rounding of P: |o - exact| <= 2^-8 sum_j P_j |v_j|
  *             before the output's own rounding (each weight rounded to nearest with 8 significant bits).
+ *             At d = 128 the weights of a query block's later key tiles are taken against the largest score
+ *             its first two tiles showed; a block whose later scores rise far enough above that to overflow
+ *             fp32 (about 2^127 in weight) is computed a second time with the running maximum at every tile,
+ *             so the result is the same either way and only the time differs.
  *             ATTN_F32 inputs run in fp32 throughout.
  *   Asynchrony Every call only enqueues work on `stream`; nothing synchronises the device.
  *   Errors    Return ATTN_OK (0) or a negative code. Argument errors are detected before anything is
