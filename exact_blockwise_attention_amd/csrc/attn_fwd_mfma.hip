@@ -268,14 +268,22 @@ __device__ __forceinline__ float weight(float s, float scale_log2, float m_use) 
 
 // The scores become exp2 weights relative to the reference, in place (fp32, kept for the row sum) and rounded to
 // bf16 in pb (the B operands of P.V, 16 keys each).
+// With `skipmax` the reference stays as it is (finite in every lane: the caller checks).
 __device__ __forceinline__ void weights_tile(float (&w)[32], bf16x8 (&pb)[4], float& m_ref, float& alpha, bool& need,
-                                             float scale_log2) {
-  // IEEE maximum (v_maximum3_f32): no NaN quieting of the MFMA results is needed before it.
-  float mx = __builtin_elementwise_maximum(w[0], w[1]);
-#pragma unroll
-  for (int e = 2; e < 32; e += 2) mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, w[e]), w[e + 1]);
+                                             float scale_log2, bool skipmax) {
   float m_use;
-  update_reference(mx, m_ref, alpha, need, m_use, scale_log2);
+  if (!skipmax) {
+    // IEEE maximum (v_maximum3_f32): no NaN quieting of the MFMA results is needed before it.
+    float mx = __builtin_elementwise_maximum(w[0], w[1]);
+#pragma unroll
+    for (int e = 2; e < 32; e += 2)
+      mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, w[e]), w[e + 1]);
+    update_reference(mx, m_ref, alpha, need, m_use, scale_log2);
+  } else {
+    alpha = 1.0f;
+    need = false;
+    m_use = m_ref;
+  }
 #pragma unroll
   for (int e = 0; e < 32; ++e) w[e] = weight(w[e], scale_log2, m_use);
 #pragma unroll
@@ -638,8 +646,36 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
     for (int ct = 0; ct < G::CT; ++ct) acc[ct] = f32x16{};
     float m_ref = -INFINITY, l_run = 0.0f;
 
-    // One tile at a time (the last tile of a wave, tiles on the diagonal, and every tile when d < 128): scores,
-    // mask, weights, rescale, P.V, sums.
+    // Speculative reference: from the third tile of a block on, the row maximum is not formed and every lane's
+    // weights are taken against the reference the first two tiles set (its rows' largest visible scores so far).
+    // Weights then come out as large as 2^(row maximum - reference) instead of at most 2^slack; in fp32 and bf16
+    // that changes no relative rounding, only the common scale of acc and l, which the epilogue divides out. Only
+    // an overflow would do harm, so the block is redone with the row maximum formed at every tile (the exact lazy
+    // rescaling above) when any wave's l or acc ends non-finite. A wave in which some lane has seen no visible
+    // key yet keeps forming the maximum.
+    bool spec = true;
+    auto skip_max = [&](int t) { return spec && t >= t0 + 2 && !__builtin_amdgcn_ballot_w64(m_ref == -INFINITY); };
+    // after the last tile: true when any wave must redo the block (every wave calls it: it holds a barrier)
+    auto must_redo = [&]() {
+      float chk = l_run;
+#pragma unroll
+      for (int ct = 0; ct < G::CT; ++ct)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) chk += acc[ct][r];
+      // every wave's copies (the last steps copy tiles no row reads) land before any wave starts over
+      wait_vmem_all();
+      return __syncthreads_or(!__builtin_isfinite(chk)) != 0;
+    };
+    auto start_over = [&]() {
+      spec = false;
+#pragma unroll
+      for (int ct = 0; ct < G::CT; ++ct) acc[ct] = f32x16{};
+      m_ref = -INFINITY;
+      l_run = 0.0f;
+      first_copies();
+    };
+
+    // One tile at a time (every tile when d < 128): scores, mask, weights, rescale, P.V, sums.
     auto plain_tile = [&](f32x16& c0, f32x16& c1, bool partial, int t, const char* vc) {
       float w[32];
       bf16x8 pb[4];
@@ -647,7 +683,7 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
       bool need;
       if (partial) mask_scores(c0, c1, row_lim - t * kBN, row_lo - t * kBN);
       unpack_scores(c0, c1, w);
-      weights_tile(w, pb, m_ref, alpha, need, a.scale_log2);
+      weights_tile(w, pb, m_ref, alpha, need, a.scale_log2, skip_max(t));
       rescale_acc<D>(acc, alpha, need);
       __builtin_amdgcn_sched_barrier(0);
       pv_tile<D, kPipe>(vc, pb, acc, la);
@@ -659,15 +695,7 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
       // weights, then P.V of tile t (V tile t) beside the rest of tile t's softmax. K tiles therefore arrive one
       // tile ahead of V tiles: after the barrier of stage t, K tile t+2 is copied into the slot of K tile t and V
       // tile t+1 into the slot of V tile t-1.
-      //
-      // Speculative reference: from the third tile of a block on, the row maximum is not formed and every lane's
-      // weights are taken against the reference the first two tiles set (its rows' largest visible scores so
-      // far). Weights then come out as large as 2^(row maximum - reference) instead of at most 2^slack; in fp32
-      // and bf16 that changes no relative rounding, only the common scale of acc and l, which the epilogue divides
-      // out. Only an overflow would do harm, so the block is redone with the row maximum formed at every tile
-      // (the exact lazy rescaling above) when any wave's l or acc ends non-finite.
       f32x16 sa0, sa1, sb0, sb1;
-      bool spec = true;
       auto stage = [&](int t, f32x16& c0, f32x16& c1, f32x16& n0, f32x16& n1, const char* kn, char* kw,
                        const char* vc, char* vw) {
         wait_vmem_all();      // this wave's copies of K tile t+1 and V tile t have landed
@@ -698,10 +726,8 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
         // so the issue arbiter favours it over the SIMD's other wave (measured: +2.5 % causal, +0.7 % unmasked).
         __builtin_amdgcn_s_setprio(1);
         bf16x8 vpre[kLead];
-        // wave-uniform; a lane whose rows have seen no visible key yet keeps the reference update
-        const bool skipmax = spec && t >= t0 + 2 && !__builtin_amdgcn_ballot_w64(m_ref == -INFINITY);
         stage_phase1<D>(kn, qf, n0, n1, la, w, pb, m_ref, alpha, need, m_use, a.scale_log2, ck, cv, vc, vpre,
-                        skipmax);
+                        skip_max(t));
         __builtin_amdgcn_s_setprio(0);
         rescale_acc<D>(acc, alpha, need);
         __builtin_amdgcn_sched_barrier(0);
@@ -715,21 +741,8 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
           stage(t, sa0, sa1, sb0, sb1, k1, k0, v0, v1);
           if (t + 1 < ntiles) stage(t + 1, sb0, sb1, sa0, sa1, k0, k1, v1, v0);
         }
-        if (!spec) break;
-        float chk = l_run;
-#pragma unroll
-        for (int ct = 0; ct < G::CT; ++ct)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) chk += acc[ct][r];
-        // every wave's copies (the last stages copy zero tiles past the end) land before any wave starts over
-        wait_vmem_all();
-        if (!__syncthreads_or(!__builtin_isfinite(chk))) break;
-        spec = false;
-#pragma unroll
-        for (int ct = 0; ct < G::CT; ++ct) acc[ct] = f32x16{};
-        m_ref = -INFINITY;
-        l_run = 0.0f;
-        first_copies();
+        if (!spec || !must_redo()) break;
+        start_over();
       }
     } else {
       // One tile per step: after the barrier of tile t, tile t+1 is copied into the slots tile t-1 left.
@@ -745,9 +758,13 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
         qk_tile<D>(kc, qf, s0, s1, la);
         plain_tile(s0, s1, t >= nfull || t < nlow, t, vc);
       };
-      for (int t = t0; t < ntiles; t += 2) {
-        step(t, k0, v0, k1, v1);
-        if (t + 1 < ntiles) step(t + 1, k1, v1, k0, v0);
+      for (;;) {
+        for (int t = t0; t < ntiles; t += 2) {
+          step(t, k0, v0, k1, v1);
+          if (t + 1 < ntiles) step(t + 1, k1, v1, k0, v0);
+        }
+        if (!spec || !must_redo()) break;
+        start_over();
       }
     }
     store_out<D, OF32, MERGE>(a, bh, q0, kRows, wave * 32 + (lane & 31), lane, acc, m_ref, l_run);
