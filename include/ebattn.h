@@ -36,7 +36,7 @@
  *             weights P are rounded to bf16 before the P.V product, and o and lse are both normalised by the sum
  *             of the fp32 weights, so o carries the bf16 rounding of P: |o - exact| <= 2^-8 sum_j P_j |v_j|
  *             before the output's own rounding (each weight rounded to nearest with 8 significant bits).
- *             At d = 128 the weights of a query block's later key tiles are taken against the largest score
+ *             On the MFMA path the weights of a query block's later key tiles are taken against the largest score
  *             its first two tiles showed; a block whose later scores rise far enough above that to overflow
  *             fp32 (about 2^127 in weight) is computed a second time with the running maximum at every tile,
  *             so the result is the same either way and only the time differs.
