@@ -39,7 +39,7 @@
  *             On the MFMA path the weights of a query block's later key tiles are taken against the largest score
  *             its first two tiles showed; a block whose later scores rise far enough above that to overflow
  *             fp32 (about 2^127 in weight) is computed a second time with the running maximum at every tile,
- *             so the result is the same either way and only the time differs.
+ *             so the bound above holds either way and only the time differs.
  *             ATTN_F32 inputs run in fp32 throughout.
  *   Asynchrony Every call only enqueues work on `stream`; nothing synchronises the device.
  *   Errors    Return ATTN_OK (0) or a negative code. Argument errors are detected before anything is
