@@ -594,6 +594,8 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
   __shared__ __attribute__((aligned(1024))) char k1[T];
   __shared__ __attribute__((aligned(1024))) char v0[T];
   __shared__ __attribute__((aligned(1024))) char v1[T];
+  __shared__ int redo_tag;   // the walk round of the last block a wave of this workgroup asked to redo
+  if (threadIdx.x == 0) redo_tag = -1;   // read only after the barriers of the first block's first tile
 
   const int lane = threadIdx.x & 63;
   // the wave index is uniform across the wave; saying so keeps every per-wave bound (and the branches on them)
@@ -655,17 +657,31 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
     // key yet keeps forming the maximum.
     bool spec = true;
     auto skip_max = [&](int t) { return spec && t >= t0 + 2 && !__builtin_amdgcn_ballot_w64(m_ref == -INFINITY); };
-    // after the last tile: true when any wave must redo the block (every wave calls it: it holds a barrier)
-    auto must_redo = [&]() {
-      float chk = l_run;
+    // After a block's last tile, in every wave (it holds the workgroup's barrier, which also tells every wave that
+    // no wave reads the LDS slots any more): true when this was the speculative pass and some wave ended it with
+    // a non-finite l or acc. The verdict travels through an LDS word tagged with the walk round, so it needs no
+    // reset; the barrier waits for LDS traffic only, not for the tile copies still in flight.
+    auto end_of_pass = [&]() {
+      const int round_tag = round;
+      // Without a merge the block's result is stored first, so that the barrier below waits while the stores
+      // drain; a redo stores it again. With a merge the running result it reads is the output, so nothing is
+      // stored before the verdict.
+      if constexpr (!MERGE) store_out<D, OF32, MERGE>(a, bh, q0, kRows, wave * 32 + (lane & 31), lane, acc, m_ref, l_run);
+      // any inf or NaN in l or acc makes the sum non-finite (four chains, short latency)
+      float part[4] = {l_run, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int ct = 0; ct < G::CT; ++ct)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) chk += acc[ct][r];
-      // every wave's copies (the last steps copy tiles no row reads) land before any wave starts over
-      wait_vmem_all();
-      return __syncthreads_or(!__builtin_isfinite(chk)) != 0;
+        for (int r = 0; r < 16; ++r) part[r & 3] += acc[ct][r];
+      const float chk = (part[0] + part[1]) + (part[2] + part[3]);
+      if (__builtin_amdgcn_ballot_w64(!__builtin_isfinite(chk)) != 0 && lane == 0) redo_tag = round_tag;
+      // the wave's LDS reads and the tag write are complete, then the barrier; written out because a fence on LDS
+      // would also wait for the tile copies into LDS still in flight, which nothing reads before the next wait
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      return spec && redo_tag == round_tag;
     };
+    // A wave's copies land in issue order and each wave fills the same rows of a slot every time, so the unused
+    // tiles the last steps copied cannot overwrite the tiles copied here.
     auto start_over = [&]() {
       spec = false;
 #pragma unroll
@@ -741,7 +757,7 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
           stage(t, sa0, sa1, sb0, sb1, k1, k0, v0, v1);
           if (t + 1 < ntiles) stage(t + 1, sb0, sb1, sa0, sa1, k0, k1, v1, v0);
         }
-        if (!spec || !must_redo()) break;
+        if (!end_of_pass()) break;
         start_over();
       }
     } else {
@@ -763,16 +779,15 @@ void attn_fwd_kernel(FwdArgs a, int n_qtiles, int xcd_remap) {
           step(t, k0, v0, k1, v1);
           if (t + 1 < ntiles) step(t + 1, k1, v1, k0, v0);
         }
-        if (!spec || !must_redo()) break;
+        if (!end_of_pass()) break;
         start_over();
       }
     }
-    store_out<D, OF32, MERGE>(a, bh, q0, kRows, wave * 32 + (lane & 31), lane, acc, m_ref, l_run);
+    if constexpr (MERGE) store_out<D, OF32, MERGE>(a, bh, q0, kRows, wave * 32 + (lane & 31), lane, acc, m_ref, l_run);
     if constexpr (!walks_blocks<D>()) break;
-    // Every wave is done reading the LDS slots (its last reads fed the products just stored) before any wave copies
-    // the next block's first tiles into them. A wave's copies land in issue order and each wave fills the same rows
-    // of a slot every time, so the unused tiles the last stages copied cannot overwrite the new ones.
-    __builtin_amdgcn_s_barrier();
+    // The barrier at the end of the block's last pass has told every wave that no wave reads the LDS slots any
+    // more, so the next block's first copies may go out now; as for a redo, the unused tiles the last steps copied
+    // cannot overwrite them.
   }
 }
 
