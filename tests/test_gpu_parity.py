@@ -145,12 +145,12 @@ def test_extreme_scores_no_overflow(eb):
         compare(host_f64(o), host_f64(lse), o_ref, l_ref, TOL_BF16, 5e-3, what=f"extreme causal={causal}")
 
 
-def _planted_key(seed, N, gain):
-    """q, k, v of N(0,1) bf16 (1 batch, 2 heads, N tokens, d = 128), with key 1300 of head 0 set to gain times
-    query 1500 of head 0: that row's score against it is about gain * 128 / sqrt(128), far above anything the
-    first two key tiles show any row."""
+def _planted_key(seed, N, gain, d=128):
+    """q, k, v of N(0,1) bf16 (1 batch, 2 heads, N tokens), with key 1300 of head 0 set to gain times query 1500 of
+    head 0: that row's score against it is about gain * sqrt(d), far above anything the first two key tiles show
+    any row."""
     from workloads import f32_to_bf16_bits
-    q, k, v = _inputs(seed, 1, 2, N, N, 128)
+    q, k, v = _inputs(seed, 1, 2, N, N, d)
     qf = bf16_bits_to_f64(q)
     k = k.copy()
     k[0, 0, 1300] = f32_to_bf16_bits((gain * qf[0, 0, 1500]).astype(np.float32))
@@ -159,20 +159,23 @@ def _planted_key(seed, N, gain):
 
 @pytest.mark.parametrize("gain", [3.0, 20.0])
 @pytest.mark.parametrize("causal", [False, True])
-def test_scores_far_above_the_first_tiles(eb, gain, causal):
-    # The pipelined kernel takes the weights of later tiles against the reference the first two tiles set. With
-    # gain 3 the planted score is about 49 (log2 units) above that reference: the weights grow to about 2^49 and
-    # stay finite. With gain 20 it is about 320 above: the weights overflow, and the block must be redone with the
-    # row maximum formed at every tile. Both must match the oracle; the fused merge of ring_local too.
+@pytest.mark.parametrize("d", [128, 64, 24])
+def test_scores_far_above_the_first_tiles(eb, gain, causal, d):
+    # The kernel takes the weights of later tiles against the reference the first two tiles set. With gain 3 the
+    # planted score is about 3 sqrt(d) (natural log) above that reference, 21 to 49 in log2 units: the weights
+    # grow to about 2^21..2^49 and stay finite. With gain 20 it is 98 to 226 (natural log) above: the weights
+    # overflow, and the block must be redone with the row maximum formed at every tile. Both must match the
+    # oracle, in the pipelined (d = 128) and the one-tile (d = 64, 24) kernels, and through the fused merge of
+    # ring_local.
     t = torch()
-    q, k, v = _planted_key(31, 2048, gain)
-    print(f"[case] planted key gain={gain} causal={causal}", flush=True)
+    q, k, v = _planted_key(31, 2048, gain, d)
+    print(f"[case] planted key gain={gain} causal={causal} d={d}", flush=True)
     o, lse = eb.attn_fwd(dev_bf16(q), dev_bf16(k), dev_bf16(v), causal=causal, out_dtype=t.float32)
     t.cuda.synchronize()
-    o_ref, l_ref = oracle.attention(bf16_bits_to_f64(q), bf16_bits_to_f64(k), bf16_bits_to_f64(v), 1 / math.sqrt(128),
+    o_ref, l_ref = oracle.attention(bf16_bits_to_f64(q), bf16_bits_to_f64(k), bf16_bits_to_f64(v), 1 / math.sqrt(d),
                                     causal=causal)
     # lse up to about 230: fp32 score rounding is ~1e-5 relative
-    compare(host_f64(o), host_f64(lse), o_ref, l_ref, TOL_BF16, 5e-3, what=f"planted gain={gain} causal={causal}")
+    compare(host_f64(o), host_f64(lse), o_ref, l_ref, TOL_BF16, 5e-3, what=f"planted gain={gain} causal={causal} d={d}")
     if causal:
         n = 512
         blocks = [(dev_bf16(np.ascontiguousarray(k[:, :, s * n:(s + 1) * n])),
@@ -181,7 +184,7 @@ def test_scores_far_above_the_first_tiles(eb, gain, causal):
                                out_dtype=t.float32)
         t.cuda.synchronize()
         compare(host_f64(o), host_f64(lse), o_ref[:, :, 3 * n:], l_ref[:, :, 3 * n:], TOL_BF16, 5e-3,
-                what=f"planted gain={gain} ring_local")
+                what=f"planted gain={gain} d={d} ring_local")
 
 
 def test_values_one_give_one(eb):
