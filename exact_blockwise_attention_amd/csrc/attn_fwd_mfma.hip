@@ -528,13 +528,13 @@ __device__ __forceinline__ void store_out(const FwdArgs& a, int64_t bh, int q0, 
 }
 
 // Workgroup -> the (batch*head slice, query block) pairs it computes, one after another. At d = 128 and 64 a
-// launch has at most walk_rounds rounds of resident workgroups, so a workgroup's start-up (Q fragment, first K/V
-// tiles, pipeline fill) and its dispatch are paid once per several blocks. Workgroups are dispatched round-robin
-// over the 8 XCDs; with the remap, workgroup b serves a contiguous range of blocks, range b mod 8, so that a
-// slice's K/V tiles are re-read from one L2. A range lists its blocks slice by slice, the heaviest causal block
-// (the last query rows) first, and deals them to its workgroups in snake order: in round r, slot s takes position
-// r*S + s when r is even and r*S + S-1-s when r is odd (S workgroups per range), which pairs heavy blocks with
-// light ones.
+// launch has at most walk_rounds rounds of resident workgroups, so a workgroup's dispatch and wave launch are
+// paid once per several blocks (each block still loads its own Q fragment and first K/V tiles). Workgroups are
+// dispatched round-robin over the 8 XCDs; with the remap, workgroup b serves a contiguous range of blocks, range
+// b mod 8, so that a slice's K/V tiles are re-read from one L2. A range lists its blocks slice by slice, the
+// heaviest causal block (the last query rows) first, and deals them to its workgroups in snake order: in round r,
+// slot s takes position r*S + s when r is even and r*S + S-1-s when r is odd (S workgroups per range), which
+// pairs heavy blocks with light ones.
 // At d = 24 the loop-carried state costs more scalar registers than the exponential-bound kernel can spare;
 // there every workgroup computes one block.
 template <int D>
