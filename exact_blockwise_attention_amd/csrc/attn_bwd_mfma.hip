@@ -728,7 +728,7 @@ void attn_bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int xcd_remap) {
   __shared__ __attribute__((aligned(1024))) char ob[G::TILE];
   __shared__ __attribute__((aligned(16))) float la_[kBT];   // exp2-domain lse of the tile rows, slot a
   __shared__ __attribute__((aligned(16))) float lb_[kBT];
-  __shared__ __attribute__((aligned(16))) float da_[kBT];   // delta of the tile rows
+  __shared__ __attribute__((aligned(16))) float da_[kBT];   // -delta of the tile rows (0 past Nq)
   __shared__ __attribute__((aligned(16))) float db_[kBT];
   __shared__ __attribute__((aligned(16))) float rla[kBT];   // raw lse and delta as copied, slots a and b
   __shared__ __attribute__((aligned(16))) float rlb[kBT];
@@ -766,7 +766,8 @@ void attn_bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int xcd_remap) {
     copy_tile<D, kBT, kW2>(Q + bh * a.Nq * D, r0, a.Nq, qd, wave, lane);
     copy_tile<D, kBT, kW2>(dO + bh * a.Nq * D, r0, a.Nq, od, wave, lane);
   };
-  // lse and delta of a stage's rows: copied raw two stages ahead and converted one stage ahead, by wave 0
+  // lse and delta of a stage's rows: copied raw two stages ahead and converted one stage ahead, by wave 0 (lse
+  // to the exp2-domain subtrahend, delta negated)
   auto issue_rows = [&](int s, float* rl, float* rd) {
     const int64_t bh = bh0 + s / nt;
     const int r0 = (t0 + s % nt) * kBT;
@@ -779,7 +780,7 @@ void attn_bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int xcd_remap) {
   auto convert_rows = [&](int s, const float* rl, const float* rd, float* lq, float* dq) {
     const int i = (t0 + s % nt) * kBT + lane;
     lq[lane] = i < a.Nq ? lse_to_sub(rl[lane]) : INFINITY;
-    dq[lane] = i < a.Nq ? rd[lane] : 0.0f;
+    dq[lane] = i < a.Nq ? -rd[lane] : 0.0f;
   };
 
   const __bf16* Ks = reinterpret_cast<const __bf16*>(a.k) + kvbh * (int64_t)a.Nk * D;
@@ -830,7 +831,18 @@ void attn_bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int xcd_remap) {
     if (wave == 0 && s + 2 < nstages) issue_rows(s + 2, rs_l, rs_d);
     const int r0 = (t0 + s % nt) * kBT + 32 * half;   // this wave's first row
     if (r0 + 31 >= any_lo && r0 <= any_hi && r0 < a.Nq) {
-      f32x16 sc = f32x16{}, dp = f32x16{};
+      // dP starts from -delta of its rows, so that it comes out of the MFMAs as dP - delta
+      f32x16 sc = f32x16{}, dp;
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int rb = 32 * half + 16 * g + 8 * hi;
+        const f32x4 d0 = *reinterpret_cast<const f32x4*>(dc + rb), d1 = *reinterpret_cast<const f32x4*>(dc + rb + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dp[8 * g + e] = d0[e];
+          dp[8 * g + 4 + e] = d1[e];
+        }
+      }
 #pragma unroll
       for (int ks = 0; ks < G::KSTEPS; ++ks) {
         sc = mfma(row_frag<D>(qc, la, half, ks), key_frag(kb, ks), sc);
@@ -850,14 +862,12 @@ void attn_bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int xcd_remap) {
       for (int g = 0; g < 2; ++g) {
         const int rb = 32 * half + 16 * g + 8 * hi;
         const f32x4 l0 = *reinterpret_cast<const f32x4*>(lc + rb), l1 = *reinterpret_cast<const f32x4*>(lc + rb + 4);
-        const f32x4 d0 = *reinterpret_cast<const f32x4*>(dc + rb), d1 = *reinterpret_cast<const f32x4*>(dc + rb + 4);
         f32x8 w, gr;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float lq = e < 4 ? l0[e] : l1[e - 4];
-          const float dl = e < 4 ? d0[e] : d1[e - 4];
           w[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * g + e], a.scale_log2, -lq));
-          gr[e] = w[e] * (dp[8 * g + e] - dl);
+          gr[e] = w[e] * dp[8 * g + e];
         }
         pb[g] = __builtin_convertvector(w, bf16x8);
         sb[g] = __builtin_convertvector(gr, bf16x8);
