@@ -106,6 +106,7 @@ __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0
 __device__ __forceinline__ void pin(bf16x8& x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin(bf16x2& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(int& x) { asm volatile("" : "+v"(x)); }
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -578,10 +579,10 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
 void attn_bwd_dkdv24_kernel(BwdArgs a, int n_ktiles, int xcd_remap) {
   static_assert(D == 24, "d = 64 and 128 take attn_bwd_dkdv_kernel");
   using G = BG<D>;
-  __shared__ __attribute__((aligned(1024))) char qa[G::TILE];
-  __shared__ __attribute__((aligned(1024))) char qb[G::TILE];
-  __shared__ __attribute__((aligned(1024))) char oa[G::TILE];
-  __shared__ __attribute__((aligned(1024))) char ob[G::TILE];
+  __shared__ __attribute__((aligned(4096))) char qa[G::TILE];
+  __shared__ __attribute__((aligned(4096))) char qb[G::TILE];
+  __shared__ __attribute__((aligned(4096))) char oa[G::TILE];
+  __shared__ __attribute__((aligned(4096))) char ob[G::TILE];
   __shared__ __attribute__((aligned(16))) float la_[kBT];   // exp2-domain lse of the tile rows, slot a
   __shared__ __attribute__((aligned(16))) float lb_[kBT];
   __shared__ __attribute__((aligned(16))) float da_[kBT];   // delta of the tile rows
@@ -720,12 +721,14 @@ void attn_bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int xcd_remap) {
   constexpr int KV = kOwn * G::RB;                // 128 key rows of K (or V)
   // Every LDS buffer is an array of its own: the compiler then knows which one a copy in flight writes, and does
   // not make the reads of the current stage's tiles wait for the copies of the next stage.
+  // The tiles' larger alignment places them first in LDS, below 64 KB, where their addresses fit the offset field
+  // of the LDS reads (only speed depends on it: elsewhere the compiler adds the address in a register).
+  __shared__ __attribute__((aligned(4096))) char qa[G::TILE];
+  __shared__ __attribute__((aligned(4096))) char qb[G::TILE];
+  __shared__ __attribute__((aligned(4096))) char oa[G::TILE];
+  __shared__ __attribute__((aligned(4096))) char ob[G::TILE];
   __shared__ __attribute__((aligned(1024))) char kb[KV];
   __shared__ __attribute__((aligned(1024))) char vb[KV];
-  __shared__ __attribute__((aligned(1024))) char qa[G::TILE];
-  __shared__ __attribute__((aligned(1024))) char qb[G::TILE];
-  __shared__ __attribute__((aligned(1024))) char oa[G::TILE];
-  __shared__ __attribute__((aligned(1024))) char ob[G::TILE];
   __shared__ __attribute__((aligned(16))) float la_[kBT];   // exp2-domain lse of the tile rows, slot a
   __shared__ __attribute__((aligned(16))) float lb_[kBT];
   __shared__ __attribute__((aligned(16))) float da_[kBT];   // -delta of the tile rows (0 past Nq)
@@ -803,8 +806,33 @@ void attn_bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int xcd_remap) {
   // 16*ks + 8*hi .. +7
   const int krow = 32 * kw + (lane & 31);
   const int koff = krow * G::RB, ksw = swz<D>(krow);
-  auto key_frag = [&](const char* t, int ks) {
-    return *reinterpret_cast<const bf16x8*>(t + koff + 16 * ((2 * ks + hi) ^ ksw));
+  // Per-lane byte offsets of every operand read of a stage, formed once and held in registers: each read is then a
+  // named buffer plus one of them, which the compiler emits with the buffer's address (and any constant part) in
+  // the instruction's offset field instead of adding addresses in the loop.
+  int keyo[G::KSTEPS], rowo[G::KSTEPS], tro[2][G::CT];
+#pragma unroll
+  for (int ks = 0; ks < G::KSTEPS; ++ks) {
+    keyo[ks] = koff + 16 * ((2 * ks + hi) ^ ksw);
+    rowo[ks] = half * 32 * G::RB + la.row_off + 16 * ((2 * ks + la.hi) ^ la.row_sw);
+    pin(keyo[ks]);
+    pin(rowo[ks]);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int ct = 0; ct < G::CT; ++ct) {
+      tro[j][ct] = 2 * half * 16 * G::RB + la.tr[j][ct];
+      pin(tro[j][ct]);
+    }
+  auto key_frag = [&](const char* t, int ks) { return *reinterpret_cast<const bf16x8*>(t + keyo[ks]); };
+  // rows 32*half + perm_row(l%32) of a tile, head-dim columns 16*ks + 8*hi .. +7
+  auto own_rows = [&](const char* t, int ks) { return *reinterpret_cast<const bf16x8*>(t + rowo[ks]); };
+  // head-dim columns 32*ct + l%32, tile rows 32*half + 16*g + 8*hi .. +7
+  auto own_tr = [&](const char* t, int g, int ct) {
+    const char* p = t + g * 16 * G::RB;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + tro[0][ct]));
+    const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + tro[1][ct]));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
   };
   const int key = kw0 + (lane & 31);
   const int vis_lo = (a.causal ? key - a.diag : -(1 << 30)) - 8 * hi;
@@ -845,8 +873,8 @@ void attn_bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int xcd_remap) {
       }
 #pragma unroll
       for (int ks = 0; ks < G::KSTEPS; ++ks) {
-        sc = mfma(row_frag<D>(qc, la, half, ks), key_frag(kb, ks), sc);
-        dp = mfma(row_frag<D>(oc, la, half, ks), key_frag(vb, ks), dp);
+        sc = mfma(own_rows(qc, ks), key_frag(kb, ks), sc);
+        dp = mfma(own_rows(oc, ks), key_frag(vb, ks), dp);
       }
       // register r holds row r0 + 16*(r/8) + 8*hi + r%8 of this lane's key
       if (!(r0 >= all_lo && r0 + 31 <= all_hi)) {
@@ -876,8 +904,8 @@ void attn_bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int xcd_remap) {
       for (int g = 0; g < 2; ++g)
 #pragma unroll
         for (int ct = 0; ct < G::CT; ++ct) {
-          dv[ct] = mfma(tr_frag<D>(oc, la, 2 * half + g, ct), pb[g], dv[ct]);
-          dk[ct] = mfma(tr_frag<D>(qc, la, 2 * half + g, ct), sb[g], dk[ct]);
+          dv[ct] = mfma(own_tr(oc, g, ct), pb[g], dv[ct]);
+          dk[ct] = mfma(own_tr(qc, g, ct), sb[g], dk[ct]);
         }
     }
     if (more && wave == 0) convert_rows(s + 1, rn_l, rn_d, ln, dn);
