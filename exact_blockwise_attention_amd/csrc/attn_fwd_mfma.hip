@@ -29,8 +29,9 @@
 //   * 64-key K and V tiles are copied HBM -> LDS by the buffer unit itself (buffer_load ... lds, 16 bytes per
 //     lane, rows past Nk read as zero), double-buffered in four separately named LDS arrays; K rows and V rows
 //     are XOR-swizzled per 16-byte chunk so that the operand reads spread over all 64 LDS banks;
-//   * 4 waves = 128 query rows per workgroup (8 waves = 256 rows for unmasked d = 128 calls), one barrier per
-//     tile; two waves share each SIMD, so one wave's softmax can also overlap the other's MFMA work.
+//   * 4 waves = 128 query rows per workgroup (8 waves = 256 rows for d = 128 calls without a mask, or with a
+//     causal mask over 16K keys or more and no window), one barrier per tile; two waves share each SIMD, so one
+//     wave's softmax can also overlap the other's MFMA work.
 #include <type_traits>
 
 #include "internal.h"
@@ -577,7 +578,10 @@ template <int D>
 constexpr bool pipelined() { return D == 128; }
 // Waves per workgroup (32 query rows each): 4 (128 rows, two workgroups per CU) or, for the pipelined kernel
 // without a causal mask, 8 (256 rows, one workgroup per CU: each K/V tile is copied into LDS once per 256 rows
-// instead of once per 128; under a causal mask the waves of such a block finish too unevenly for it to pay).
+// instead of once per 128). The larger block draws less power per FLOP, so the part holds a higher clock, but its
+// eight waves share one barrier per tile, and under a causal mask the diagonal tiles leave some of them idle.
+// Measured on three parts: with 16K keys or more per call (long rows, relatively few diagonal tiles) it is 0.4-2.6 %
+// faster; at 8K keys and with a sliding window it is within -2 and +2.5 % by part, so those keep 4 waves.
 
 template <int D, bool OF32, int NW, bool MERGE>
 __global__ __launch_bounds__(64 * NW)
@@ -814,7 +818,7 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
 template <int D, bool OF32>
 hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
   if constexpr (pipelined<D>()) {
-    if (!a.causal) return launch_d<D, OF32, 8>(a, stream);
+    if (!a.causal || (a.lo == kNoWindow && a.Nk >= 16384)) return launch_d<D, OF32, 8>(a, stream);
   }
   return launch_d<D, OF32, 4>(a, stream);
 }
