@@ -5,7 +5,8 @@ The query rows sit at the end of the keys (bottom-right, as a ring shard's rows 
 diagonal tiles, and both lengths are ragged against the 256-row blocks and 64-key tiles. Each case runs with and
 without a planted key whose score for one row overflows the weights taken against the first two tiles' maximum:
 that block must be computed again with the row maximum formed at every tile. The fused merge of ring_local runs
-the same kernel with a running result. Tolerances (max-abs): bf16 paths 2e-2 on o, lse 1e-3 (5e-3 with the
+the same kernel with a running result; grouped query heads run it over a shared key/value head (and, with a
+sliding window, the 4-wave kernel). Tolerances (max-abs): bf16 paths 2e-2 on o, lse 1e-3 (5e-3 with the
 planted score, whose lse is about 230).
 """
 import math
@@ -97,3 +98,21 @@ def test_long_causal_bf16_out(eb):
     o_ref, l_ref = oracle.attention(bf16_bits_to_f64(q), bf16_bits_to_f64(k), bf16_bits_to_f64(v), 1 / math.sqrt(D),
                                     causal=True, q_off=16200)
     compare(host_f64(o), host_f64(lse), o_ref, l_ref, TOL_BF16, TOL_LSE, what="long causal bf16 out")
+
+
+@pytest.mark.parametrize("window", [0, 4096], ids=["grouped", "grouped_window"])
+def test_long_causal_grouped_heads(eb, window):
+    # four query heads over one key/value head, 16500 keys: without a window the 8-wave kernel, with one the
+    # 4-wave kernel (both must agree with the oracle)
+    t = torch()
+    Nq, Nk, q_off = 300, 16500, 16200
+    print(f"[case] long causal grouped heads window={window}", flush=True)
+    q = normal_bf16_bits(53, "q", (1, 4, Nq, D))
+    k = normal_bf16_bits(53, "k", (1, 1, Nk, D))
+    v = normal_bf16_bits(53, "v", (1, 1, Nk, D))
+    o, lse = eb.attn_fwd_ex(dev_bf16(q), dev_bf16(k), dev_bf16(v), causal=True, q_off=q_off, window=window,
+                            out_dtype=t.float32)
+    t.cuda.synchronize()
+    o_ref, l_ref = oracle.attention(bf16_bits_to_f64(q), bf16_bits_to_f64(k), bf16_bits_to_f64(v), 1 / math.sqrt(D),
+                                    causal=True, q_off=q_off, window=window)
+    compare(host_f64(o), host_f64(lse), o_ref, l_ref, TOL_BF16, TOL_LSE, what=f"long causal grouped window={window}")
