@@ -1,7 +1,8 @@
 """Benchmark of the exact blockwise attention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu] [--no-counters] [--copy-probe BYTES]
-                    [--merge-only | --bwd-only | --rows-only | --profile {fwd,bwd,merge,rows} --profile-out DIR]
+                    [--merge-only | --bwd-only | --rows-only | --long-only
+                     | --profile {fwd,bwd,merge,rows,long} --profile-out DIR]
 
 A step is one attention forward (scores, causal mask by position, online softmax, P.V, epilogue) over the
 causal self-attention workload B=4, H=32, N=8192, d=128, bf16 in / bf16 out with fp32 lse, inputs iid N(0,1)
@@ -411,19 +412,19 @@ def bench_ring_pipeline(torch, eb, dev, c3, qd, kd, vd, order, ms_compute, fl, s
             "hidden_fraction_of_copies": (ms_compute + ms_copy - ms_pipe) / ms_copy}
 
 
-def bench_long(torch, eb, dev, steps):
+def bench_long(torch, eb, dev, steps, keys=("causal_32k", "causal_128k"), exact_steps=False):
     """Single-call causal self-attention at the long end of the 8K..128K range: B=1, H=32, d=128, N = 32768 and
-    131072 (the whole sequence on one GPU, no ring)."""
+    131072 (the whole sequence on one GPU, no ring). exact_steps: time exactly `steps` calls (profiling)."""
     from workloads import CONFIGS, normal_bf16_bits
     from workloads import accounting as acc
     out = {}
-    for key in ("causal_32k", "causal_128k"):
+    for key in keys:
         c = CONFIGS[key]
         q, k, v = (upload_bf16(normal_bf16_bits(c.seed, t, (c.B, c.H, c.Nq, c.d)), torch, dev) for t in "qkv")
         o = torch.empty_like(q)
         lse = torch.empty((c.B, c.H, c.Nq), dtype=torch.float32, device=dev)
-        ms = time_region(torch, lambda: eb.attn_fwd(q, k, v, scale=c.scale, causal=True, out=o, lse=lse),
-                         max(2, steps // 4) if c.Nq > 40000 else max(steps, 10), 1)
+        n_timed = steps if exact_steps else (max(2, steps // 4) if c.Nq > 40000 else max(steps, 10))
+        ms = time_region(torch, lambda: eb.attn_fwd(q, k, v, scale=c.scale, causal=True, out=o, lse=lse), n_timed, 1)
         fl = acc.attention_flops(acc.config_pairs(c), c.d)
         out[key] = {"ms": ms, "TFLOP/s": fl / ms / 1e9, "frac_mfma_peak": fl / ms / 1e9 / PEAK_BF16_TFLOPS}
         del q, k, v, o, lse
@@ -586,6 +587,7 @@ PROFILE_TARGETS = {
     "bwd": (["--bwd-only"], ["attn_bwd_dq_kernel<128", "attn_bwd_dkdv_kernel<128"], 10, 2),
     "merge": (["--merge-only"], ["lse_merge_kernel"], 20, 3),
     "rows": (["--rows-only"], ["attn_fwd_kernel<24"], 4, 1),
+    "long": (["--long-only"], ["attn_fwd_kernel<128"], 4, 1),
 }
 
 
@@ -726,8 +728,11 @@ PROFILE_SUMMARY = {
     "bwd": "attention backward, causal self-attention B=4 H=32 N=8192 d=128 (bf16 q, k, v, dout; fp32 dq, dk, dv)",
     "merge": "LSE merge of two fp32 partials in place, 1,048,576 rows x d=128 (the ring-share shape)",
     "rows": "tabular row axis, 8 x 4 sequences of 150000 tokens, d=24, non-causal (bf16 in and out)",
+    "long": "attention forward, one causal call over N=131072, B=1 H=32 d=128 (8-wave workgroups; bf16 q, k, v, o; "
+            "fp32 lse)",
 }
-SOURCES = {"fwd": "attn_fwd_mfma.hip", "bwd": "attn_bwd_mfma.hip", "merge": "lse_merge.hip", "rows": "attn_fwd_mfma.hip"}
+SOURCES = {"fwd": "attn_fwd_mfma.hip", "bwd": "attn_bwd_mfma.hip", "merge": "lse_merge.hip", "rows": "attn_fwd_mfma.hip",
+           "long": "attn_fwd_mfma.hip"}
 
 
 def source_hash(name):
@@ -742,6 +747,10 @@ def profile_accounting(kind):
     from workloads import accounting as acc
     if kind == "fwd":
         c = CONFIGS["causal_8k"]
+        return {"attn_fwd_kernel<128": (acc.attention_flops(acc.config_pairs(c), c.d),
+                                        acc.attn_fwd_bytes(c.B, c.H, c.Nq, c.Nq, c.d, 2, 2), "algorithmic")}
+    if kind == "long":
+        c = CONFIGS["causal_128k"]
         return {"attn_fwd_kernel<128": (acc.attention_flops(acc.config_pairs(c), c.d),
                                         acc.attn_fwd_bytes(c.B, c.H, c.Nq, c.Nq, c.d, 2, 2), "algorithmic")}
     if kind == "rows":
@@ -836,6 +845,9 @@ def main(argv=None):
                     help="time only the attention backward (for profiling it) and print its figures as one JSON line")
     ap.add_argument("--rows-only", action="store_true",
                     help="time only the tabular row axis (d = 24) and print its figures as one JSON line")
+    ap.add_argument("--long-only", action="store_true",
+                    help="time only the causal call over N = 131072 (exactly --steps calls) and print its figures "
+                         "as one JSON line")
     ap.add_argument("--no-counters", action="store_true",
                     help="skip the rocprofv3 passes (kernel trace, SQ counters) over a child run of the headline step")
     ap.add_argument("--profile", choices=sorted(PROFILE_TARGETS),
@@ -881,6 +893,9 @@ def main(argv=None):
         return 0
     if args.rows_only:
         print(json.dumps(bench_tabular(torch, eb, dev, args.steps, rows_only=True)), flush=True)
+        return 0
+    if args.long_only:
+        print(json.dumps(bench_long(torch, eb, dev, args.steps, keys=("causal_128k",), exact_steps=True)), flush=True)
         return 0
     cfg = CONFIGS["causal_8k"]
     t0 = time.perf_counter()
