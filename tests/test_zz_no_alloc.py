@@ -54,6 +54,7 @@ def _call_noalloc(eb, qd, blocks, o, lse, q_off):
 @pytest.mark.parametrize("dtype,shapes", [
     ("bf16", [(1, 8, 1000, 4, 128), (1, 2, 300, 3, 64)]),
     ("f32", [(1, 4, 500, 3, 128), (1, 1, 130, 2, 24)]),
+    ("bf16", [(1, 2, 16500, 2, 128), (1, 1, 300, 2, 128)]),   # blocks over 16K keys: the 8-wave causal kernel
 ])
 def test_noalloc_matches_ring_local_twice(eb, dtype, shapes):
     t = torch()
