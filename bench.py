@@ -853,7 +853,8 @@ def main(argv=None):
     ap.add_argument("--profile", choices=sorted(PROFILE_TARGETS),
                     help="only run the rocprofv3 passes (trace, SQ counters, HBM traffic) of one step kind into "
                          "--profile-out and print their figures as one JSON line")
-    ap.add_argument("--profile-out", default=os.path.join(ROOT, "gpurun_out", "profile"))
+    ap.add_argument("--profile-out", default=os.path.join(os.environ.get("TMPDIR", "/tmp"), "ebattn_profile"),
+                    help="directory for the raw rocprofv3 output of --profile")
     ap.add_argument("--profile-summary", default=None,
                     help="with --profile: also write the figures as a text summary to this path")
     args = ap.parse_args(argv)
