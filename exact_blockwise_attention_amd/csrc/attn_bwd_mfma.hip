@@ -329,6 +329,11 @@ void attn_bwd_dq_kernel(BwdArgs a, int n_qtiles, int xcd_remap) {
   f32x16 acc[G::CT];
 #pragma unroll
   for (int ct = 0; ct < G::CT; ++ct) acc[ct] = f32x16{};
+  // -delta of the lane's row in every register: the dP products start from it, so they give dP - delta and the
+  // score gradient needs one multiply per element
+  f32x16 negd;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) negd[r] = -dl;
 
   auto step = [&](int t, const char* kc, const char* vc, char* kn, char* vn) {
     wait_vmem_all();      // this wave's copies of tile t have landed
@@ -338,13 +343,13 @@ void attn_bwd_dq_kernel(BwdArgs a, int n_qtiles, int xcd_remap) {
       copy_tile<D>(V, (t + 1) * kBT, a.Nk, vn, wave, lane);
     }
     if (t >= nt_w) return;
-    f32x16 s0 = f32x16{}, s1 = f32x16{}, p0 = f32x16{}, p1 = f32x16{};
+    f32x16 s0 = f32x16{}, s1 = f32x16{}, p0, p1;
 #pragma unroll
     for (int ks = 0; ks < G::KSTEPS; ++ks) {
       s0 = mfma(row_frag<D>(kc, la, 0, ks), qf[ks], s0);
       s1 = mfma(row_frag<D>(kc, la, 1, ks), qf[ks], s1);
-      p0 = mfma(row_frag<D>(vc, la, 0, ks), df[ks], p0);
-      p1 = mfma(row_frag<D>(vc, la, 1, ks), df[ks], p1);
+      p0 = mfma(row_frag<D>(vc, la, 0, ks), df[ks], ks == 0 ? negd : p0);
+      p1 = mfma(row_frag<D>(vc, la, 1, ks), df[ks], ks == 0 ? negd : p1);
     }
     // register r of s0/s1 holds key 32*h + 16*(r/8) + 8*hi + r%8 of the tile (h = 0/1)
     if (t >= nfull || t < nlow) {
@@ -366,7 +371,7 @@ void attn_bwd_dq_kernel(BwdArgs a, int n_qtiles, int xcd_remap) {
         const float sv = (kk >> 1) ? s1[r] : s0[r];
         const float pv = (kk >> 1) ? p1[r] : p0[r];
         const float pw = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, a.scale_log2, -lsub));
-        x[e] = pw * (pv - dl);
+        x[e] = pw * pv;   // pv is dP - delta
       }
       db[kk] = __builtin_convertvector(x, bf16x8);
     }
