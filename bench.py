@@ -723,7 +723,7 @@ def profile_kind(kind, outdir, traffic=False, limit_s=240):
 
 
 PROFILE_SUMMARY = {
-    # kind -> (title, kernel source, (kernel substring, label, flop, algorithmic bytes) per kernel)
+    # kind -> title of its summary
     "fwd": "attention forward, causal self-attention B=4 H=32 N=8192 d=128 (bf16 q, k, v, o; fp32 lse)",
     "bwd": "attention backward, causal self-attention B=4 H=32 N=8192 d=128 (bf16 q, k, v, dout; fp32 dq, dk, dv)",
     "merge": "LSE merge of two fp32 partials in place, 1,048,576 rows x d=128 (the ring-share shape)",
